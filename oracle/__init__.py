@@ -1,0 +1,28 @@
+"""Float64 CPU oracle for the Ulysses per-rank attention path.
+
+TEST INFRASTRUCTURE ONLY. This package is the slow, plain definition that the
+GPU path is checked against. Only the test suite, the package smoke check and
+the benchmark's CPU-baseline leg may import it; the product path never does,
+and this package imports nothing from the product package.
+
+Contents:
+  permute    seq-sharded <-> head-sharded layout change of sp virtual ranks
+             (the data movement of Ulysses' all-to-alls), by slicing.
+  attention  exact softmax attention (causal or not, packed documents kept
+             apart) forward with its log-sum-exp, and the analytic backward,
+             in float64 with whole-row normalisation.
+
+Every function here is pinned by tests that do not call it twice: closed
+forms, finite differences, brute-force loops, an independent library
+(torch float64 SDPA) and the invariants the pages state.
+"""
+
+from .permute import seq_to_head, head_to_seq  # noqa: F401
+from .attention import (  # noqa: F401
+    attn_fwd,
+    attn_bwd,
+    attn_fwd_rows,
+    attn_bwd_dq_rows,
+    attn_bwd_dkdv_cols,
+    doc_ids,
+)
