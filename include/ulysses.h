@@ -1,0 +1,136 @@
+/*
+ * ulysses.h -- C ABI of the per-rank hot path of Ulysses sequence parallelism
+ * on MI355X (gfx950).
+ *
+ * What the operations are (sources are the pages' titles and sections):
+ *   - HF Transformers docs, "Ulysses sequence parallelism" (deepspeed_alst),
+ *     opening paragraph and layout diagram: sp ranks each hold N/sp tokens of
+ *     all H heads; an all-to-all moves them to all N tokens of H/sp heads per
+ *     rank; attention runs there; a second all-to-all moves back.
+ *   - congresoia365 article "Nuevo método Ulysses ...", section "Cómo Funciona
+ *     Ulysses": the local attention is the standard mechanism, and heads are
+ *     independent of one another.
+ *   - The same guide, "sp_attn_implementation" paragraph: samples packed into
+ *     one row must not attend across their boundaries.
+ *   - congresoia365 article, section "El Desafío del Entrenamiento de
+ *     Secuencias Largas": memory-efficient attention keeps O(N) state and
+ *     never stores the N x N score matrix.
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is device memory owned by the caller, contiguous
+ *     and row-major in the layout stated at the call. The library keeps no
+ *     state, allocates no memory, and is safe to call from several host
+ *     threads on different streams.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns; results are ready when
+ *     the stream is.
+ *   - Arguments are checked on the host before anything is enqueued; a call
+ *     that returns an error has enqueued nothing. The contents of device
+ *     buffers (e.g. cu_seqlens) are never read on the host.
+ *   - dtype is ULY_F32 (float) or ULY_BF16 (bfloat16, round-to-nearest-even
+ *     outputs). Accumulation is always in fp32.
+ *   - Head width d must be 64 or 128.
+ */
+#ifndef ULYSSES_H
+#define ULYSSES_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define ULY_OK 0
+#define ULY_EINVAL 1       /* null pointer where one is required, or a size <= 0 */
+#define ULY_ESHAPE 2       /* N % sp != 0, H % sp != 0, or an inconsistent size */
+#define ULY_EUNSUPPORTED 3 /* dtype not ULY_F32/ULY_BF16, or d not in {64, 128} */
+#define ULY_EWORKSPACE 4   /* workspace pointer NULL or smaller than required */
+#define ULY_EHIP 5         /* the HIP runtime refused a launch */
+
+/* Element types. */
+#define ULY_F32 0
+#define ULY_BF16 1
+
+/*
+ * Layout change of all-to-all #1 (sequence-sharded -> head-sharded) for sp
+ * virtual ranks held on one device (guide, layout diagram, upper half).
+ *   x_seq  [sp][B][N/sp][H][d]   shard s holds tokens [s*N/sp, (s+1)*N/sp) of all H heads
+ *   x_head [sp][B][N][H/sp][d]   shard r holds all N tokens of heads [r*H/sp, (r+1)*H/sp)
+ *   x_head[r][b][s*N/sp + t][h][:] = x_seq[s][b][t][r*H/sp + h][:]
+ * N is the full sequence length. Elements are copied as raw bits (bit-exact,
+ * NaN payloads and -0 kept). x_seq and x_head must not overlap.
+ * Errors: ULY_EINVAL (null, size <= 0), ULY_ESHAPE (N % sp, H % sp),
+ * ULY_EUNSUPPORTED (dtype, d), ULY_EHIP.
+ */
+int ulysses_seq_to_head(const void* x_seq, void* x_head, int B, int N, int H, int d, int sp,
+                        int dtype, void* stream);
+
+/*
+ * Layout change of all-to-all #2 (head-sharded -> sequence-sharded), the
+ * inverse of ulysses_seq_to_head (guide, layout diagram, lower half). It is
+ * also the backward of ulysses_seq_to_head (the transpose of a permutation is
+ * its inverse), and ulysses_seq_to_head is the backward of this call.
+ *   x_head [sp][B][N][H/sp][d]  ->  x_seq [sp][B][N/sp][H][d]
+ * Same argument meaning and errors as ulysses_seq_to_head.
+ */
+int ulysses_head_to_seq(const void* x_head, void* x_seq, int B, int N, int H, int d, int sp,
+                        int dtype, void* stream);
+
+/*
+ * Attention forward over the head-sharded shares of sp virtual ranks
+ * (congresoia365 article, "Cómo Funciona Ulysses", local attention step).
+ * For every (rank, batch row, head), with scale = 1/sqrt(d):
+ *   S = scale * Q K^T, masked to allowed(i, j) = same document and
+ *   (causal == 0 or j <= i); O = softmax_rows(S) V;
+ *   lse_i = ln sum_{allowed j} exp(S_ij).
+ *   q, k, v, o  [sp][B][N][Hl][d] of dtype; o is fully overwritten.
+ *   lse         [sp][B][Hl][N] float (natural log), fully overwritten; it is
+ *               the only state the backward needs besides the inputs.
+ *   cu_seqlens  device int32 [ndoc+1], cu[0] = 0, non-decreasing,
+ *               cu[ndoc] = N: document boundaries shared by every row; or
+ *               NULL for one document [0, N) per row (ndoc, max_doc_len
+ *               ignored). Empty documents are allowed.
+ *   max_doc_len host int >= the longest document (sizes the launch; a
+ *               smaller value leaves rows uncomputed).
+ * Errors: ULY_EINVAL (null pointer, size <= 0, ndoc < 1 or max_doc_len < 1
+ * with cu_seqlens), ULY_ESHAPE (max_doc_len > N), ULY_EUNSUPPORTED, ULY_EHIP.
+ */
+int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B, int N,
+                     int Hl, int d, int causal, int dtype, void* stream);
+
+/*
+ * Bytes of device workspace ulysses_attn_bwd needs: one float per (rank,
+ * batch row, head, token), i.e. O(N), never O(N^2). Returns 0 for invalid
+ * arguments.
+ */
+size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype);
+
+/*
+ * Attention backward (the adjoint of ulysses_attn_fwd). With P recomputed
+ * tile by tile from lse, D_i = sum_c dO_ic O_ic and the same mask:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   q, k, v, o, dout  [sp][B][N][Hl][d] of dtype (o and lse from the forward)
+ *   lse               [sp][B][Hl][N] float
+ *   dq, dk, dv        [sp][B][N][Hl][d] of dtype, fully overwritten
+ *   workspace         device memory of workspace_bytes >=
+ *                     ulysses_attn_bwd_workspace_bytes(...); contents on
+ *                     entry are ignored, on return unspecified.
+ * cu_seqlens, ndoc, max_doc_len, causal as in ulysses_attn_fwd.
+ * Errors: as ulysses_attn_fwd, plus ULY_EWORKSPACE.
+ */
+int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len,
+                     int sp, int B, int N, int Hl, int d, int causal, int dtype, void* stream);
+
+/* Static English text for a status code (never NULL). */
+const char* ulysses_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ULYSSES_H */

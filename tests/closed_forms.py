@@ -19,6 +19,12 @@ from __future__ import annotations
 import math
 
 import numpy as np
+import torch
+
+
+def _cumsum0(x):
+    """Prefix sums along axis 0 (float64; torch's CPU kernel is much faster than numpy's here)."""
+    return torch.from_numpy(np.array(x, dtype=np.float64, order="C", copy=True)).cumsum(0).numpy()
 
 
 def _bounds(N, cu):
@@ -40,7 +46,7 @@ def q0_forward(v1, cu=None, causal=True):
             continue
         if causal:
             n = np.arange(1, L + 1, dtype=np.float64)
-            O[s:e] = np.cumsum(v[s:e], axis=0) / n[:, None]
+            O[s:e] = _cumsum0(v[s:e]) / n[:, None]
             lse[s:e] = np.log(n)
         else:
             O[s:e] = v[s:e].mean(axis=0)
@@ -67,16 +73,16 @@ def q0_backward(k1, v1, do1, cu=None, causal=True, block=256):
         if causal:
             n = np.arange(1, L + 1, dtype=np.float64)
             g = do[s:e] / n[:, None]
-            dv[s:e] = np.cumsum(g[::-1], axis=0)[::-1]
-            ksum = np.cumsum(k[s:e], axis=0)
-            M = np.zeros((d, d))
+            dv[s:e] = _cumsum0(g[::-1])[::-1]
+            ksum = _cumsum0(k[s:e])
+            M = np.zeros((d, d))  # sum over earlier blocks of k_j v_j^T
             for a in range(0, L, block):
                 b = min(L, a + block)
-                outer = k[s + a:s + b, :, None] * v[s + a:s + b, None, :]
-                Mi = M[None] + np.cumsum(outer, axis=0)  # sum_{j<=i} k_j v_j^T
-                M = Mi[-1]
-                t1 = np.einsum("icd,id->ic", Mi, do[s + a:s + b])
+                Kb, Vb, Gb = k[s + a:s + b], v[s + a:s + b], do[s + a:s + b]
+                T = np.tril(Gb @ Vb.T)  # T[i, j] = dO_i . v_j for block-local j <= i
+                t1 = Gb @ M.T + T @ Kb  # (sum_{j<=i} k_j v_j^T) dO_i
                 dq[s + a:s + b] = scale / n[a:b, None] * (t1 - D[s + a:s + b, None] * ksum[a:b])
+                M += Kb.T @ Vb
         else:
             dv[s:e] = do[s:e].sum(axis=0) / L
             M = k[s:e].T @ v[s:e]

@@ -1,0 +1,107 @@
+"""The C-ABI library loads, exports every declared call, and rejects bad
+arguments on the host before enqueuing anything (CPU only: no call here
+reaches a kernel launch)."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import ulysses_sequence_parallelism_seq_amd as uly
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ulysses.h")
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation first
+OK, EINVAL, ESHAPE, EUNSUP, EWS = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ulysses_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = uly.library()
+    names = declared_functions()
+    assert set(names) == {
+        "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
+        "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string",
+    }
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(6):
+        assert uly.ulysses_status_string(code)
+    assert uly.ulysses_status_string(99) == "unknown status"
+
+
+def test_permute_argument_errors():
+    lib = uly.library()
+    f = lib.ulysses_seq_to_head
+    assert f(None, FAKE, 1, 8, 4, 64, 2, 1, None) == EINVAL
+    assert f(FAKE, FAKE, 0, 8, 4, 64, 2, 1, None) == EINVAL
+    assert f(FAKE, ctypes.c_void_p(0x100000), 1, 9, 4, 64, 2, 1, None) == ESHAPE  # N % sp
+    assert f(FAKE, ctypes.c_void_p(0x100000), 1, 8, 5, 64, 2, 1, None) == ESHAPE  # H % sp
+    assert f(FAKE, ctypes.c_void_p(0x100000), 1, 8, 4, 96, 2, 1, None) == EUNSUP  # d
+    assert f(FAKE, ctypes.c_void_p(0x100000), 1, 8, 4, 64, 2, 7, None) == EUNSUP  # dtype
+    # overlapping buffers
+    assert f(FAKE, ctypes.c_void_p(0x1000 + 64), 1, 8, 4, 64, 2, 1, None) == EINVAL
+    g = lib.ulysses_head_to_seq
+    assert g(FAKE, ctypes.c_void_p(0x100000), 1, 6, 4, 64, 4, 1, None) == ESHAPE
+
+
+def test_attention_argument_errors():
+    lib = uly.library()
+    fwd = lib.ulysses_attn_fwd
+    args = dict(cu=None, ndoc=1, maxlen=8, sp=1, B=1, N=8, Hl=2, d=64, causal=1, dtype=1)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return fwd(FAKE, FAKE, FAKE, FAKE, FAKE, a["cu"], a["ndoc"], a["maxlen"], a["sp"], a["B"], a["N"],
+                   a["Hl"], a["d"], a["causal"], a["dtype"], None)
+
+    assert fwd(None, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
+    assert call(N=0) == EINVAL
+    assert call(d=32) == EUNSUP
+    assert call(dtype=3) == EUNSUP
+    assert call(cu=FAKE, ndoc=0) == EINVAL
+    assert call(cu=FAKE, maxlen=9) == ESHAPE
+
+    bwd = lib.ulysses_attn_bwd
+    need = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 64, 1)
+    assert need == 1 * 1 * 2 * 8 * 4
+    assert lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 48, 1) == 0
+    ptrs = [FAKE] * 9
+    assert bwd(*ptrs, FAKE, need - 1, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert bwd(*ptrs, None, need, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert bwd(*ptrs[:8], None, FAKE, need, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
+    assert bwd(*ptrs, FAKE, need, None, 1, 8, 1, 1, 8, 2, 64, 1, 9, None) == EUNSUP
+
+
+def test_workspace_is_linear_in_n():
+    lib = uly.library()
+    w1 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 131072, 4, 128, 1)
+    w2 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 262144, 4, 128, 1)
+    assert w2 == 2 * w1 == 2 * 131072 * 4 * 4
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        uly.ulysses_seq_to_head(torch.zeros(2, 1, 4, 4, 64, dtype=torch.bfloat16),
+                                out=torch.zeros(2, 1, 8, 2, 64, dtype=torch.bfloat16))
+
+
+def test_binding_validates_cu_seqlens():
+    for bad in ([0, 5], [1, 8], [0, 6, 3, 8]):
+        with pytest.raises(ValueError):
+            uly.DocPacking(bad, 8, "cpu")
+    p = uly.DocPacking([0, 3, 3, 8], 8, "cpu")
+    assert (p.ndoc, p.max_doc_len) == (3, 5)

@@ -1,0 +1,185 @@
+"""GPU parity against the float64 oracle, element by element, at sizes the
+oracle finishes in seconds: several tiles, ragged tails, packed documents
+(including empty and one-token ones), both head widths, causal and not."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+import ulysses_sequence_parallelism_seq_amd as uly
+from tests.gpu_util import (TOL_BF16_GRAD, TOL_BF16_O, TOL_F32_ABS, assert_abs, assert_rel, device, f64,
+                            say)
+
+pytestmark = pytest.mark.gpu
+
+
+# ------------------------------------------------------------------ permute
+
+
+@pytest.mark.parametrize("sp,B,Ns,H,d,dtype", [
+    (2, 1, 128, 4, 64, "fp32"),     # tiny workload's shards
+    (4, 2, 1024, 32, 128, "bf16"),  # llama7b workload's shards (full size)
+    (3, 2, 7, 6, 64, "bf16"),
+    (1, 1, 5, 2, 128, "fp32"),
+    (8, 1, 33, 16, 128, "bf16"),
+])
+def test_permute_bit_exact(sp, B, Ns, H, d, dtype):
+    say("permute", sp, B, Ns, H, d, dtype)
+    dev = device()
+    x = workloads.random_bits((sp, B, Ns, H, d), seed=11 + sp, dtype=dtype)
+    ibits = torch.int16 if dtype == "bf16" else torch.int32
+    head = uly.ulysses_seq_to_head(x.to(dev))
+    torch.cuda.synchronize()
+    want = oracle.seq_to_head(x.view(ibits).numpy())
+    assert np.array_equal(head.cpu().view(ibits).numpy(), want)
+    back = uly.ulysses_head_to_seq(head)
+    torch.cuda.synchronize()
+    assert np.array_equal(back.cpu().view(ibits).numpy(), x.view(ibits).numpy())
+    y = workloads.random_bits((sp, B, Ns * sp, H // sp, d), seed=5, dtype=dtype)
+    seq = uly.ulysses_head_to_seq(y.to(dev))
+    torch.cuda.synchronize()
+    assert np.array_equal(seq.cpu().view(ibits).numpy(), oracle.head_to_seq(y.view(ibits).numpy()))
+
+
+# ------------------------------------------------------------ fp32 exactness
+
+
+def _run_gpu(q, k, v, do, cu, causal):
+    dev = device()
+    qd, kd, vd, dod = (t.to(dev) for t in (q, k, v, do))
+    o, lse = uly.ulysses_attn_fwd(qd, kd, vd, cu, causal)
+    dq, dk, dv = uly.ulysses_attn_bwd(qd, kd, vd, o, dod, lse, cu, causal)
+    torch.cuda.synchronize()
+    return o.cpu(), lse.cpu(), dq.cpu(), dk.cpu(), dv.cpu()
+
+
+def test_tiny_fp32_exact():
+    """The tiny workload: B=1, N=256, 2 local heads of width 64, fp32, causal."""
+    w = workloads.WORKLOADS["tiny"]
+    say("tiny fp32", w)
+    q, k, v, do = workloads.qkv_do((1, w.B, w.N, w.Hl, w.d), w.seed, "fp32")
+    o, lse, dq, dk, dv = _run_gpu(q, k, v, do, None, True)
+    O, L = oracle.attn_fwd(q, k, v)
+    G = oracle.attn_bwd(q, k, v, do)
+    assert_abs(o, O, TOL_F32_ABS, "O")
+    assert_abs(lse, L, TOL_F32_ABS, "lse")
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), G):
+        assert_abs(got, want, TOL_F32_ABS, name)
+
+
+@pytest.mark.parametrize("N,Hl,d,causal,lengths", [
+    (300, 2, 128, False, [1, 150, 0, 149]),
+    (200, 1, 64, True, [70, 130]),
+    (65, 3, 64, False, None),
+])
+def test_fp32_shapes(N, Hl, d, causal, lengths):
+    say("fp32", N, Hl, d, causal, lengths)
+    cu = None if lengths is None else workloads.cu_seqlens_from_lengths(lengths)
+    q, k, v, do = workloads.qkv_do((2, 1, N, Hl, d), 21, "fp32")
+    o, lse, dq, dk, dv = _run_gpu(q, k, v, do, cu, causal)
+    O, L = oracle.attn_fwd(q, k, v, cu, causal)
+    G = oracle.attn_bwd(q, k, v, do, cu, causal)
+    assert_abs(o, O, TOL_F32_ABS, "O")
+    assert_abs(lse, L, TOL_F32_ABS, "lse")
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), G):
+        assert_abs(got, want, TOL_F32_ABS, name)
+
+
+def test_tiny_stitched_virtual_ranks():
+    """Full-H sequence shards -> seq_to_head -> per-rank attention -> head_to_seq on
+    the GPU equals the oracle's attention over all heads of the unsharded sequence."""
+    w = workloads.WORKLOADS["tiny"]
+    say("tiny stitched", w)
+    dev = device()
+    full = workloads.qkv_do((w.B, w.N, w.H, w.d), w.seed, "fp32")  # [B, N, H, d]
+    shards = [x.view(w.B, w.sp, w.Ns, w.H, w.d).permute(1, 0, 2, 3, 4).contiguous() for x in full]
+    heads = [uly.ulysses_seq_to_head(s.to(dev)) for s in shards]
+    o, lse = uly.ulysses_attn_fwd(heads[0], heads[1], heads[2])
+    dq, dk, dv = uly.ulysses_attn_bwd(heads[0], heads[1], heads[2], o, heads[3], lse)
+    outs = [uly.ulysses_head_to_seq(t) for t in (o, dq, dk, dv)]
+    torch.cuda.synchronize()
+    O, _ = oracle.attn_fwd(*full[:3])
+    G = oracle.attn_bwd(*full)
+    for name, got, want in zip(("O", "dQ", "dK", "dV"), outs, (O,) + G):
+        got_full = got.cpu().permute(1, 0, 2, 3, 4).reshape(w.B, w.N, w.H, w.d)
+        assert_abs(got_full, want, TOL_F32_ABS, name)
+
+
+# -------------------------------------------------------------- bf16 MFMA
+
+
+BF16_CASES = [
+    # (sp, B, N, Hl, d, causal, lengths)
+    (1, 2, 1000, 2, 128, True, None),
+    (1, 1, 1000, 2, 64, True, [300, 0, 1, 699]),
+    (1, 1, 777, 3, 128, False, [129, 128, 520]),
+    (2, 1, 640, 2, 128, True, [5, 200, 435]),
+    (1, 1, 97, 1, 128, True, None),
+    (1, 1, 1, 1, 128, True, None),
+    (1, 1, 513, 2, 64, False, None),
+    (1, 1, 384, 4, 128, True, [128, 128, 128]),
+    (1, 1, 1200, 1, 128, True, [1] * 50 + [1150]),
+]
+
+
+@pytest.mark.parametrize("sp,B,N,Hl,d,causal,lengths", BF16_CASES)
+def test_bf16_parity(sp, B, N, Hl, d, causal, lengths):
+    say("bf16", sp, B, N, Hl, d, causal, lengths)
+    cu = None if lengths is None else workloads.cu_seqlens_from_lengths(lengths)
+    q, k, v, do = workloads.qkv_do((sp, B, N, Hl, d), 31 + N, "bf16")
+    o, lse, dq, dk, dv = _run_gpu(q, k, v, do, cu, causal)
+    O, L = oracle.attn_fwd(q, k, v, cu, causal)
+    G = oracle.attn_bwd(q, k, v, do, cu, causal)
+    assert_rel(o, O, TOL_BF16_O, "O")
+    assert_abs(lse, L, 1e-3, "lse")
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), G):
+        assert_rel(got, want, TOL_BF16_GRAD, name)
+
+
+def test_bf16_packed_equals_separate():
+    """Guide, sp_attn_implementation: packed documents give the same result as each run alone."""
+    say("bf16 packed == separate")
+    lengths = [200, 1, 311, 0, 88]
+    cu = workloads.cu_seqlens_from_lengths(lengths)
+    N = sum(lengths)
+    q, k, v, do = workloads.qkv_do((1, 1, N, 2, 128), 77, "bf16")
+    packed = _run_gpu(q, k, v, do, cu, True)
+    for s, e in zip(cu[:-1], cu[1:]):
+        if s == e:
+            continue
+        alone = _run_gpu(*(t[:, :, s:e].contiguous() for t in (q, k, v, do)), None, True)
+        for name, a, b in zip(("O", "dQ", "dK", "dV"), (packed[0], *packed[2:]), (alone[0], *alone[2:])):
+            assert torch.equal(a[:, :, s:e], b), name
+        assert torch.equal(packed[1][..., s:e], alone[1]), "lse"
+
+
+def test_bf16_bitwise_reproducible():
+    say("bf16 reproducible")
+    q, k, v, do = workloads.qkv_do((1, 1, 1500, 2, 128), 5, "bf16")
+    r1 = _run_gpu(q, k, v, do, None, True)
+    r2 = _run_gpu(q, k, v, do, None, True)
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_bf16_constant_v_and_zero_q():
+    """Closed forms: constant v gives O = v and dQ = dK = 0 (up to rounding);
+    q = 0 gives O_i = mean of v over keys 0..i and lse_i = ln(i + 1)."""
+    say("bf16 closed forms small")
+    N, d = 700, 128
+    dev = device()
+    q, k, v, do = workloads.qkv_do((1, 1, N, 1, d), 8, "bf16")
+    vc = v[:, :, :1].expand(1, 1, N, 1, d).contiguous()
+    o, lse, dq, dk, dv = _run_gpu(q, k, vc, do, None, True)
+    assert_rel(o, vc, 1e-2, "O const v")
+    assert np.abs(f64(dq)).max() < 1e-2 * np.abs(f64(do)).max()
+    z = torch.zeros_like(q)
+    o, lse, dq, dk, dv = _run_gpu(z, k, v, do, None, True)
+    want = np.cumsum(f64(v)[0, 0, :, 0], axis=0) / np.arange(1, N + 1)[:, None]
+    assert_rel(o[0, 0, :, 0], want, TOL_BF16_O, "O q=0")
+    np.testing.assert_allclose(f64(lse)[0, 0, 0], np.log(np.arange(1, N + 1)), atol=1e-4)
+    assert torch.count_nonzero(dk) == 0

@@ -1,0 +1,223 @@
+"""Ulysses sequence parallelism, per-rank hot path on MI355X (gfx950).
+
+A thin Python binding over the C-ABI library ``libulysses.so`` (declared in
+``include/ulysses.h``). It only marshals arguments: torch tensors become
+device pointers, torch's current HIP stream becomes the launch stream, and
+output tensors are allocated with torch. Every step of the computation runs
+in the library's HIP kernels; there is no CPU or eager fallback, and a
+missing library is an error.
+
+Functions carry the C names:
+  ulysses_seq_to_head(x_seq, sp)          [sp,B,N/sp,H,d] -> [sp,B,N,H/sp,d]
+  ulysses_head_to_seq(x_head, sp)         [sp,B,N,H/sp,d] -> [sp,B,N/sp,H,d]
+  ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)
+  ulysses_attn_bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)
+  ulysses_attn_bwd_workspace_bytes(...), ulysses_status_string(code)
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libulysses.so")
+
+ULY_F32, ULY_BF16 = 0, 1
+_DTYPES = {torch.float32: ULY_F32, torch.bfloat16: ULY_BF16}
+
+_lib = None
+
+
+class UlyssesError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        super().__init__(f"{fn} failed with status {code}: {ulysses_status_string(code)}")
+
+
+def library() -> ctypes.CDLL:
+    """The loaded C-ABI library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m ulysses_sequence_parallelism_seq_amd.build`"
+            )
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        lib.ulysses_seq_to_head.argtypes = [vp, vp, i, i, i, i, i, i, vp]
+        lib.ulysses_head_to_seq.argtypes = [vp, vp, i, i, i, i, i, i, vp]
+        lib.ulysses_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
+        lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+        lib.ulysses_attn_bwd_workspace_bytes.restype = sz
+        lib.ulysses_attn_bwd.argtypes = [vp] * 10 + [sz, vp] + [i] * 9 + [vp]
+        lib.ulysses_status_string.argtypes = [i]
+        lib.ulysses_status_string.restype = ctypes.c_char_p
+        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd"):
+            getattr(lib, name).restype = i
+        _lib = lib
+    return _lib
+
+
+def ulysses_status_string(code: int) -> str:
+    return library().ulysses_status_string(int(code)).decode()
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise UlyssesError(fn, code)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype not in _DTYPES:
+        raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
+    return _DTYPES[t.dtype]
+
+
+def _require_device(*ts):
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU (the HIP path has no CPU fallback)")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _expect(t: torch.Tensor, shape, dtype, name: str):
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {tuple(shape)} {dtype}, got {tuple(t.shape)} {t.dtype}")
+
+
+def ulysses_seq_to_head(x_seq: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[sp, B, N/sp, H, d] sequence shards -> [sp, B, N, H/sp, d] head shards (bit-exact)."""
+    sp, B, Ns, H, d = x_seq.shape
+    if H % sp:
+        raise ValueError("H must be divisible by sp")
+    if out is None:
+        out = torch.empty((sp, B, Ns * sp, H // sp, d), dtype=x_seq.dtype, device=x_seq.device)
+    _expect(out, (sp, B, Ns * sp, H // sp, d), x_seq.dtype, "out")
+    _require_device(x_seq, out)
+    _check("ulysses_seq_to_head", library().ulysses_seq_to_head(
+        _ptr(x_seq), _ptr(out), B, Ns * sp, H, d, sp, _dtype_code(x_seq), _stream(x_seq)))
+    return out
+
+
+def ulysses_head_to_seq(x_head: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """[sp, B, N, H/sp, d] head shards -> [sp, B, N/sp, H, d] sequence shards (bit-exact)."""
+    sp, B, N, Hl, d = x_head.shape
+    if N % sp:
+        raise ValueError("N must be divisible by sp")
+    if out is None:
+        out = torch.empty((sp, B, N // sp, Hl * sp, d), dtype=x_head.dtype, device=x_head.device)
+    _expect(out, (sp, B, N // sp, Hl * sp, d), x_head.dtype, "out")
+    _require_device(x_head, out)
+    _check("ulysses_head_to_seq", library().ulysses_head_to_seq(
+        _ptr(x_head), _ptr(out), B, N, Hl * sp, d, sp, _dtype_code(x_head), _stream(x_head)))
+    return out
+
+
+class DocPacking:
+    """Document boundaries (cu_seqlens) checked on the host and held on the device."""
+
+    def __init__(self, cu_seqlens, N: int, device):
+        cu = np.asarray(cu_seqlens.cpu() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens).reshape(-1)
+        cu = cu.astype(np.int64)
+        if len(cu) < 2 or cu[0] != 0 or cu[-1] != N or np.any(np.diff(cu) < 0):
+            raise ValueError("cu_seqlens must start at 0, be non-decreasing and end at N")
+        self.ndoc = len(cu) - 1
+        self.max_doc_len = int(np.diff(cu).max())
+        self.host = cu.astype(np.int32)
+        self.device_tensor = torch.from_numpy(self.host).to(device)
+
+
+def _packing(cu_seqlens, N, device):
+    if cu_seqlens is None:
+        return None, 1, N
+    p = cu_seqlens if isinstance(cu_seqlens, DocPacking) else DocPacking(cu_seqlens, N, device)
+    return p.device_tensor, p.ndoc, p.max_doc_len
+
+
+def _share_shape(q: torch.Tensor):
+    if q.dim() == 4:  # one rank: [B, N, Hl, d]
+        return (1,) + tuple(q.shape)
+    if q.dim() == 5:  # stacked virtual ranks: [sp, B, N, Hl, d]
+        return tuple(q.shape)
+    raise ValueError("q must be [B, N, Hl, d] or [sp, B, N, Hl, d]")
+
+
+def ulysses_attn_fwd(q, k, v, cu_seqlens=None, causal: bool = True, out=None, lse=None):
+    """Attention forward over head-sharded shares; returns (o, lse).
+
+    q, k, v: [sp, B, N, Hl, d] or [B, N, Hl, d]; lse is [..., Hl, N] float32.
+    cu_seqlens: None, host int sequence / tensor, or a DocPacking.
+    """
+    sp, B, N, Hl, d = _share_shape(q)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must share shape and dtype")
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty(tuple(q.shape[:-3]) + (Hl, N), dtype=torch.float32, device=q.device)
+    _expect(out, q.shape, q.dtype, "out")
+    _expect(lse, tuple(q.shape[:-3]) + (Hl, N), torch.float32, "lse")
+    _require_device(q, k, v, out, lse)
+    cu_dev, ndoc, maxlen = _packing(cu_seqlens, N, q.device)
+    _check("ulysses_attn_fwd", library().ulysses_attn_fwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_dev), ndoc, maxlen,
+        sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
+    return out, lse
+
+
+def ulysses_attn_bwd_workspace_bytes(sp: int, B: int, N: int, Hl: int, d: int, dtype: torch.dtype) -> int:
+    return int(library().ulysses_attn_bwd_workspace_bytes(sp, B, N, Hl, d, _DTYPES[dtype]))
+
+
+def ulysses_attn_bwd(q, k, v, o, dout, lse, cu_seqlens=None, causal: bool = True, workspace=None,
+                     dq=None, dk=None, dv=None):
+    """Attention backward; returns (dq, dk, dv) with q's shape and dtype."""
+    sp, B, N, Hl, d = _share_shape(q)
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must share shape and dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    need = ulysses_attn_bwd_workspace_bytes(sp, B, N, Hl, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _expect(lse, tuple(q.shape[:-3]) + (Hl, N), torch.float32, "lse")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, q.shape, q.dtype, name)
+    _require_device(q, k, v, o, dout, lse, dq, dk, dv, workspace)
+    cu_dev, ndoc, maxlen = _packing(cu_seqlens, N, q.device)
+    _check("ulysses_attn_bwd", library().ulysses_attn_bwd(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(cu_dev), ndoc, maxlen,
+        sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
+    return dq, dk, dv
+
+
+__all__ = [
+    "DocPacking",
+    "UlyssesError",
+    "library",
+    "ulysses_seq_to_head",
+    "ulysses_head_to_seq",
+    "ulysses_attn_fwd",
+    "ulysses_attn_bwd",
+    "ulysses_attn_bwd_workspace_bytes",
+    "ulysses_status_string",
+]

@@ -1,0 +1,355 @@
+// Attention forward on gfx950 matrix cores (bf16 inputs, fp32 accumulation),
+// and the ulysses_attn_fwd entry point.
+//
+// What it computes (congresoia365 article, "Cómo Funciona Ulysses": each rank
+// runs standard attention over all N tokens of its heads; HF guide,
+// "sp_attn_implementation": packed samples stay apart; congresoia365,
+// "El Desafío ...": O(N) memory, no N x N matrix): for every (row, head),
+// O = softmax(Q K^T / sqrt(d) + mask) V and lse = ln sum exp(...), with the
+// mask allowing key j for query i iff both sit in the same document and
+// (not causal or j <= i).
+//
+// Kernel design (one workgroup = 4 waves = a tile of 128 queries of one
+// document of one (row, head)):
+//   * Each wave owns 32 queries. It computes S^T = K Q^T with the 32x32x16
+//     bf16 MFMA: K (A operand) comes from LDS, Q^T (B operand) stays in
+//     registers for the whole kernel. In the S^T accumulator layout a lane
+//     holds one query and 16 keys, so row max and row sum are in-register
+//     except for one exchange between the two half-waves.
+//   * Online softmax in the exp2 domain (log2(e)/sqrt(d) folded into one
+//     multiply). P^T is packed to bf16 straight from the accumulator and is
+//     the B operand of O^T += V^T P^T, again a 32x32x16 MFMA, with V^T read
+//     from LDS. The MFMA k index is mapped to keys so that each lane's own
+//     P values form its B operand (no data movement between lanes). The O^T
+//     accumulator has one query per lane, so the rescale by the running-max
+//     correction is a per-lane scalar.
+//   * K/V tiles of 64 keys are staged in LDS (K row-major, V transposed),
+//     double-buffered: the global loads of tile t+1 are issued before the
+//     math of tile t and written to the other buffer after it, one barrier
+//     per tile.
+//   * Documents: a query tile never straddles a document; its keys run from
+//     the document start to the tile's last query (causal) or the document
+//     end. Only the tiles that cross the diagonal or the document end are
+//     masked element by element.
+//   * Launch order: query-tile index descending (longest causal work first),
+//     then document, then (row, head). Workgroups are dealt round-robin to
+//     the 8 XCDs, so with (row, head) fastest each XCD keeps to a few heads
+//     and its L2 serves their K/V tiles to all the XCD's workgroups.
+
+#include <math.h>
+
+#include "common.h"
+#include "launch.h"
+
+namespace {
+
+using namespace uly;
+
+constexpr int kBQ = 128;  // queries per workgroup
+constexpr int kBK = 64;   // keys per K/V tile
+constexpr int kThreads = 256;
+
+template <int D>
+struct FwdSmem {
+  static constexpr int KS = D + 8;    // K row stride (bf16): conflict-free 16-byte reads
+  static constexpr int VS = kBK + 4;  // V^T row stride (bf16): conflict-free 8-byte reads
+  static constexpr int K_ELEMS = kBK * KS;
+  static constexpr int V_ELEMS = D * VS;
+  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  static constexpr int BYTES = 2 * STAGE * 2;
+};
+
+struct FwdArgs {
+  const bf16* q;
+  const bf16* k;
+  const bf16* v;
+  bf16* o;
+  float* lse;
+  const int* cu;
+  int ndoc;
+  int nq_slots;  // query tiles per document slot
+  int units;     // G * Hl
+  int Hl;
+  int N;
+  int causal;
+  float sl2;  // log2(e) / sqrt(d)
+};
+
+// Global -> register staging of one K/V tile (rows >= e are zero).
+template <int D>
+struct TileRegs {
+  static constexpr int KCH = kBK * D / 8 / kThreads;                 // 16-byte K chunks per thread
+  static constexpr int VBL = (kBK / 4) * (D / 8);                    // 4x8 V blocks per tile
+  static constexpr int VPT = (VBL + kThreads - 1) / kThreads;        // per thread
+  uint4 kr[KCH];
+  uint4 vr[VPT][4];
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const bf16* kb, const bf16* vb, size_t rs,
+                                          int kt0, int e, int tid) {
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
+    const int id = tid + j * kThreads;
+    const int key = id / (D / 8), c8 = id % (D / 8);
+    const int row = kt0 + key;
+    r.kr[j] = row < e ? *reinterpret_cast<const uint4*>(kb + (size_t)row * rs + c8 * 8) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::VPT; ++j) {
+    const int id = tid + j * kThreads;
+    if (id < TileRegs<D>::VBL) {
+      const int kg = id % (kBK / 4), cg = id / (kBK / 4);
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int row = kt0 + 4 * kg + x;
+        r.vr[j][x] = row < e ? *reinterpret_cast<const uint4*>(vb + (size_t)row * rs + cg * 8)
+                             : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16* vs, int tid) {
+  using S = FwdSmem<D>;
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
+    const int id = tid + j * kThreads;
+    const int key = id / (D / 8), c8 = id % (D / 8);
+    *reinterpret_cast<uint4*>(ks + key * S::KS + c8 * 8) = r.kr[j];
+  }
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::VPT; ++j) {
+    const int id = tid + j * kThreads;
+    if (id < TileRegs<D>::VBL) {
+      const int kg = id % (kBK / 4), cg = id / (kBK / 4);
+      // 4 keys x 8 columns -> 8 rows of V^T with 4 consecutive keys each.
+      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.vr[j][0]);
+      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.vr[j][1]);
+      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.vr[j][2]);
+      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.vr[j][3]);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const int wi = c >> 1;
+        uint32_t lo, hi;
+        if (c & 1) {
+          lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+          hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+        } else {
+          lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+          hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+        }
+        *reinterpret_cast<uint2*>(vs + (cg * 8 + c) * S::VS + kg * 4) = make_uint2(lo, hi);
+      }
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+  using S = FwdSmem<D>;
+  constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
+  constexpr int CB = D / 32;  // 32-wide column blocks of O^T
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * S::STAGE];
+
+  // ---- which tile
+  const int per_level = a.ndoc * a.units;
+  const int lvl = blockIdx.x / per_level;
+  const int rem = blockIdx.x - lvl * per_level;
+  const int doc = rem / a.units;
+  const int unit = rem - doc * a.units;
+  const int qslot = a.nq_slots - 1 - lvl;
+  int s = 0, e = a.N;
+  if (a.cu) {
+    s = a.cu[doc];
+    e = a.cu[doc + 1];
+  }
+  const int q0 = s + qslot * kBQ;
+  if (q0 >= e) return;  // the whole workgroup leaves before any barrier
+
+  const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
+  const size_t rs = (size_t)a.Hl * D;
+  const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
+  const bf16* qb = a.q + base;
+  const bf16* kb = a.k + base;
+  const bf16* vb = a.v + base;
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int qi = q0 + 32 * w + l32;  // this lane's query
+  const bool qvalid = qi < e;
+
+  // ---- Q^T operand, resident for the whole kernel
+  uint4 qreg[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    qreg[kk] = qvalid ? *reinterpret_cast<const uint4*>(qb + (size_t)qi * rs + 16 * kk + 8 * half)
+                      : make_uint4(0, 0, 0, 0);
+
+  const int kend = a.causal ? min(e, q0 + kBQ) : e;
+  const int ntiles = (kend - s + kBK - 1) / kBK;
+
+  f32x16 oacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
+
+  TileRegs<D> tr;
+  load_tile<D>(tr, kb, vb, rs, s, e, tid);
+  store_tile<D>(tr, smem, smem + S::K_ELEMS, tid);
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt0 = s + t * kBK;
+    const bf16* ks = smem + (t & 1) * S::STAGE;
+    const bf16* vs = ks + S::K_ELEMS;
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile<D>(tr, kb, vb, rs, kt0 + kBK, e, tid);
+
+    const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
+    if (wave_active) {
+      // S^T for two 32-key blocks
+      f32x16 sacc[2];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const uint4 av = *reinterpret_cast<const uint4*>(ks + (blk * 32 + l32) * S::KS + 16 * kk + 8 * half);
+          sacc[blk] = mfma32(as_bf16x8(av), as_bf16x8(qreg[kk]), sacc[blk]);
+        }
+      }
+      // scale to the log2 domain, mask where the tile crosses the diagonal or the document end
+      const bool need_mask = (a.causal && kt0 + kBK - 1 > q0) || kt0 + kBK > e;
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float x = sacc[blk][i] * a.sl2;
+          if (need_mask) {
+            const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (key >= e || (a.causal && key > qi)) x = -INFINITY;
+          }
+          sacc[blk][i] = x;
+          mloc = fmaxf(mloc, x);
+        }
+      mloc = fmaxf(mloc, swap_halves(mloc));
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+
+      // P^T = exp2(x - m), packed to bf16 as the B operand of four 16-key MFMA steps
+      uint4 pb[4];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          float p[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            p[j] = fast_exp2(sacc[blk][8 * mm + j] - m_run);
+            l_run += p[j];
+          }
+          pb[blk * 2 + mm] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+        }
+
+      // O^T += V^T P^T. MFMA k index 8*half + j of step (blk, mm) is key
+      // blk*32 + 16*mm + 4*half + j (j < 4) or blk*32 + 16*mm + 8 + 4*half + (j - 4).
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const bf16* vrow = vs + (cb * 32 + l32) * S::VS + 4 * half;
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const int koff = (st >> 1) * 32 + (st & 1) * 16;
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + koff);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + koff + 8);
+          oacc[cb] = mfma32(as_bf16x8(make_bf16x8_bits(lo, hi)), as_bf16x8(pb[st]), oacc[cb]);
+        }
+      }
+    }
+
+    if (more) store_tile<D>(tr, smem + ((t + 1) & 1) * S::STAGE, smem + ((t + 1) & 1) * S::STAGE + S::K_ELEMS, tid);
+    __syncthreads();
+  }
+
+  // ---- normalise and write O (one query per lane, 4 consecutive columns per store) and lse
+  const float l_tot = l_run + swap_halves(l_run);
+  if (qvalid) {
+    const float inv = 1.f / l_tot;
+    bf16* orow = a.o + base + (size_t)qi * rs;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int c = cb * 32 + 8 * gq + 4 * half;
+        *reinterpret_cast<uint2*>(orow + c) = pack4_scaled(oacc[cb], 4 * gq, inv);
+      }
+    if (half == 0) a.lse[(size_t)unit * a.N + qi] = (m_run + log2f(l_tot)) * kLn2;
+  }
+}
+
+}  // namespace
+
+namespace uly_host {
+
+int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const AttnGeom& g, void* stream) {
+  FwdArgs a;
+  a.q = static_cast<const bf16*>(q);
+  a.k = static_cast<const bf16*>(k);
+  a.v = static_cast<const bf16*>(v);
+  a.o = static_cast<bf16*>(o);
+  a.lse = lse;
+  a.cu = g.cu;
+  a.ndoc = g.ndoc;
+  const int maxlen = g.cu ? g.max_doc_len : g.N;
+  a.nq_slots = (maxlen + kBQ - 1) / kBQ;
+  a.units = g.G * g.Hl;
+  a.Hl = g.Hl;
+  a.N = g.N;
+  a.causal = g.causal;
+  a.sl2 = uly::kLog2e / sqrtf((float)g.d);
+  const long long blocks = (long long)a.nq_slots * a.ndoc * a.units;
+  if (blocks > 0x7fffffffLL) return ULY_ESHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (g.d == 64)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  return launch_status();
+}
+
+}  // namespace uly_host
+
+extern "C" int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B,
+                                int N, int Hl, int d, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ULY_EINVAL;
+  const int rc = uly_host::check_attn_args(ndoc, max_doc_len, cu_seqlens, sp, B, N, Hl, d, dtype);
+  if (rc != ULY_OK) return rc;
+  uly_host::AttnGeom g;
+  g.G = sp * B;
+  g.N = N;
+  g.Hl = Hl;
+  g.d = d;
+  g.cu = cu_seqlens;
+  g.ndoc = cu_seqlens ? ndoc : 1;
+  g.max_doc_len = cu_seqlens ? max_doc_len : N;
+  g.causal = causal ? 1 : 0;
+  if (dtype == ULY_F32)
+    return uly_host::launch_attn_fwd_f32(static_cast<const float*>(q), static_cast<const float*>(k),
+                                         static_cast<const float*>(v), static_cast<float*>(o), lse, g,
+                                         stream);
+  return uly_host::launch_attn_fwd_bf16(q, k, v, o, lse, g, stream);
+}

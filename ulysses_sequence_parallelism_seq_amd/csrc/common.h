@@ -1,0 +1,84 @@
+// Shared helpers of the gfx950 kernels: vector types, MFMA wrappers, host-side
+// argument checks and launch error mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ulysses.h"
+
+namespace uly {
+
+typedef __bf16 bf16;
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 32x32x16 bf16 MFMA, fp32 accumulate. Lane l (h = l / 32) supplies
+// A[m = l % 32][k = 8h .. 8h+7] and B[k = 8h .. 8h+7][n = l % 32]; the result
+// element acc[i] of lane l is C[m = 8(i/4) + 4h + (i%4)][n = l % 32].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ uint4 make_bf16x8_bits(uint2 lo, uint2 hi) {
+  return make_uint4(lo.x, lo.y, hi.x, hi.y);
+}
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low|high.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16 a = (bf16)lo;
+  bf16 b = (bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Elements i0 .. i0+3 of an accumulator, times s, as four packed bf16.
+__device__ __forceinline__ uint2 pack4_scaled(const f32x16& v, int i0, float s) {
+  return make_uint2(pack_bf16x2(v[i0] * s, v[i0 + 1] * s), pack_bf16x2(v[i0 + 2] * s, v[i0 + 3] * s));
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
+  return __builtin_bit_cast(float, bits16 << 16);
+}
+
+// Value held by lane (l ^ 32) of the wave.
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
+
+// exp2 on the hardware transcendental unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace uly
+
+// ---------------------------------------------------------------- host side
+
+namespace uly_host {
+
+inline bool dtype_ok(int dtype) { return dtype == ULY_F32 || dtype == ULY_BF16; }
+inline bool head_dim_ok(int d) { return d == 64 || d == 128; }
+inline size_t elem_size(int dtype) { return dtype == ULY_F32 ? 4 : 2; }
+
+inline int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? ULY_OK : ULY_EHIP;
+}
+
+// Checks shared by the attention calls.
+inline int check_attn_args(int ndoc, int max_doc_len, const int* cu, int sp, int B, int N, int Hl,
+                           int d, int dtype) {
+  if (sp <= 0 || B <= 0 || N <= 0 || Hl <= 0 || d <= 0) return ULY_EINVAL;
+  if (!dtype_ok(dtype) || !head_dim_ok(d)) return ULY_EUNSUPPORTED;
+  if (cu) {
+    if (ndoc < 1 || max_doc_len < 1) return ULY_EINVAL;
+    if (max_doc_len > N) return ULY_ESHAPE;
+  }
+  // Token and element offsets are formed in 64 bits; launch sizes in 32.
+  if ((long long)sp * B * Hl > (1LL << 24)) return ULY_ESHAPE;
+  return ULY_OK;
+}
+
+}  // namespace uly_host
