@@ -1,0 +1,248 @@
+"""Benchmark of the Ulysses per-rank hot path on one MI355X.
+
+One step = one Ulysses attention layer, forward and backward, for all sp
+virtual ranks of the workload held on this GPU (default: the long-context
+workload, B=1, N=131072, H=32, sp=8, d=128, bf16, causal):
+  seq_to_head(q), (k), (v)          8 shards [16384, 32, 128] -> 8 shares [131072, 4, 128]
+  attn_fwd over the 8 shares         saves lse only
+  head_to_seq(o), seq_to_head(dO)
+  attn_bwd over the 8 shares         D pre-pass + dK/dV + dQ kernels
+  head_to_seq(dq), (dk), (dv)
+Inputs are seeded synthetic tensors already resident in HBM. Every call is
+timed with HIP events on the stream it runs on.
+
+value = causal attention FLOPs counted as 14 * d * pairs (4 d forward, 10 d
+backward; pairs = sum over documents of L (L + 1) / 2 per row and head)
+divided by the whole step's time, in TFLOP/s.
+
+Prints one JSON line. --gpus above 1 exits: this build measures one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+import torch
+
+import workloads
+import ulysses_sequence_parallelism_seq_amd as uly
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
+PEAK_HBM_GBS = 8000.0
+
+
+def causal_pairs(w: workloads.Workload) -> int:
+    cu = workloads.workload_cu_seqlens(w)
+    lengths = [w.N] if cu is None else np.diff(cu).tolist()
+    if w.causal:
+        return sum(L * (L + 1) // 2 for L in lengths)
+    return sum(L * L for L in lengths)
+
+
+def make_inputs(w: workloads.Workload, dev):
+    """Full-H sequence shards of q, k, v, dO drawn on the device from one seeded generator."""
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    shape = workloads.seq_shard_shape(w)
+    out = []
+    for _ in range(4):
+        x = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+        if w.scale != 1.0:
+            x.mul_(w.scale)
+        out.append(x.to(workloads.torch_dtype(w.dtype)))
+        del x
+    return out
+
+
+class Timer:
+    """HIP-event timing of each named call over the timed steps."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.pending = []
+
+    def run(self, name, fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        out = fn()
+        b.record(self.stream)
+        self.pending.append((name, a, b))
+        return out
+
+    def averages(self):
+        acc = {}
+        for name, a, b in self.pending:
+            acc.setdefault(name, []).append(a.elapsed_time(b))
+        return {k: statistics.mean(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+
+
+def step(w, bufs, packing, timer=None):
+    run = timer.run if timer else (lambda name, fn: fn())
+    qs, ks, vs, dos = bufs["seq_in"]
+    qh, kh, vh, doh = bufs["head_in"]
+    o, lse, dq, dk, dv = bufs["head_out"]
+    os_, dqs, dks, dvs = bufs["seq_out"]
+    ws = bufs["ws"]
+    run("seq_to_head", lambda: uly.ulysses_seq_to_head(qs, out=qh))
+    run("seq_to_head", lambda: uly.ulysses_seq_to_head(ks, out=kh))
+    run("seq_to_head", lambda: uly.ulysses_seq_to_head(vs, out=vh))
+    run("attn_fwd", lambda: uly.ulysses_attn_fwd(qh, kh, vh, packing, w.causal, out=o, lse=lse))
+    run("head_to_seq", lambda: uly.ulysses_head_to_seq(o, out=os_))
+    run("seq_to_head", lambda: uly.ulysses_seq_to_head(dos, out=doh))
+    run("attn_bwd", lambda: uly.ulysses_attn_bwd(qh, kh, vh, o, doh, lse, packing, w.causal, workspace=ws,
+                                                 dq=dq, dk=dk, dv=dv))
+    run("head_to_seq", lambda: uly.ulysses_head_to_seq(dq, out=dqs))
+    run("head_to_seq", lambda: uly.ulysses_head_to_seq(dk, out=dks))
+    run("head_to_seq", lambda: uly.ulysses_head_to_seq(dv, out=dvs))
+
+
+def cpu_baseline(w: workloads.Workload, target_s: float):
+    """The float64 oracle, fwd + bwd, on the causal prefix of one head (bounded sample)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=os.cpu_count())
+    except Exception:  # threadpoolctl missing: report the visible cores
+        threads = os.cpu_count()
+
+    def run(M):
+        q, k, v, do = workloads.qkv_do((1, M, 1, w.d), w.seed, w.dtype, w.scale)
+        t0 = time.perf_counter()
+        oracle.attn_fwd(q, k, v, None, True)
+        oracle.attn_bwd(q, k, v, do, None, True)
+        return time.perf_counter() - t0
+
+    M = 2048
+    t = run(M)
+    # cost grows as M^2: pick the prefix that takes about target_s
+    M2 = int(M * (target_s / max(t, 1e-3)) ** 0.5) // 256 * 256
+    M2 = max(2048, min(M2, w.N))
+    if M2 != M:
+        M, t = M2, run(M2)
+    flops = 14 * w.d * (M * (M + 1) // 2)
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"float64 oracle fwd+bwd of one head, causal prefix of {M} of the {w.N} tokens "
+                  f"({t:.1f} s; FLOPs counted as 14*d*pairs like the GPU value)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="long", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus > 1 or world > 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); "
+              "the sequence-parallel exchange across GPUs is not part of this build", file=sys.stderr)
+        sys.exit(2)
+
+    w = workloads.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cu = workloads.workload_cu_seqlens(w)
+    packing = None if cu is None else uly.DocPacking(cu, w.N, dev)
+
+    seq_in = make_inputs(w, dev)
+    head_shape = (w.sp, w.B, w.N, w.Hl, w.d)
+    dt = workloads.torch_dtype(w.dtype)
+    bufs = {
+        "seq_in": seq_in,
+        "head_in": [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(4)],
+        "head_out": [torch.empty(head_shape, dtype=dt, device=dev),
+                     torch.empty((w.sp, w.B, w.Hl, w.N), dtype=torch.float32, device=dev)]
+                    + [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(3)],
+        "seq_out": [torch.empty_like(seq_in[0]) for _ in range(4)],
+        "ws": torch.empty(uly.ulysses_attn_bwd_workspace_bytes(w.sp, w.B, w.N, w.Hl, w.d, dt),
+                          dtype=torch.uint8, device=dev),
+    }
+    stream = torch.cuda.current_stream(dev)
+
+    for _ in range(args.warmup):
+        step(w, bufs, packing)
+    torch.cuda.synchronize()
+
+    timer = Timer(stream)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(w, bufs, packing, timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg, counts = timer.averages()
+
+    ms_per_step = elapsed * 1e3 / args.steps
+    pairs = causal_pairs(w) * w.sp * w.B * w.Hl  # all virtual ranks, batch rows, local heads
+    flops_step = 14 * w.d * pairs
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    attn_ms = avg["attn_fwd"] + avg["attn_bwd"]
+    esize = 2 if w.dtype == "bf16" else 4
+    tensor_bytes = w.B * w.N * w.H * w.d * esize
+    permute_gbs = 2 * tensor_bytes / (statistics.mean([avg["seq_to_head"], avg["head_to_seq"]]) * 1e-3) / 1e9
+    bwd_tflops = 10 * w.d * pairs / (avg["attn_bwd"] * 1e-3) / 1e12
+    fwd_tflops = 4 * w.d * pairs / (avg["attn_fwd"] * 1e-3) / 1e12
+
+    result = {
+        "metric": "causal attn fwd+bwd TFLOP/s per GPU (% bf16 MFMA peak); permute GB/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v/dO on the device)",
+        "config": {
+            "workload": f"{w.name}: B={w.B} N={w.N} H={w.H} sp={w.sp} (all {w.sp} virtual ranks on one GPU) "
+                        f"Hl={w.Hl} d={w.d} {w.dtype} causal={w.causal} docs={w.docs}",
+            "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "attn_fwd_ms": round(avg["attn_fwd"], 3),
+            "attn_bwd_ms": round(avg["attn_bwd"], 3),
+            "attn_fwd_tflops": round(fwd_tflops, 1),
+            "attn_bwd_tflops": round(bwd_tflops, 1),
+            "attn_only_tflops": round(flops_step / (attn_ms * 1e-3) / 1e12, 1),
+            "permute_ms": round(statistics.mean([avg["seq_to_head"], avg["head_to_seq"]]), 4),
+            "permute_gbs": round(permute_gbs, 1),
+            "permute_pct_of_hbm_peak": round(100 * permute_gbs / PEAK_HBM_GBS, 1),
+            "flops_per_step": flops_step,
+            "calls_timed": counts,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "attn_bwd (D pre-pass + dK/dV + dQ kernels of one ulysses_attn_bwd call)",
+            "achieved": round(bwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -105,13 +105,11 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
 // ----------------------------------------------------------- shared tile staging
 // A 4-token x 8-column block of a [token][d] tensor, loaded as four 16-byte
 // rows; written to LDS row-major and/or transposed ([column][token]).
-__device__ __forceinline__ void load_block4(uint4 (&r)[4], const bf16* base, size_t rs, int row0, int c8,
-                                            int e) {
+// off0 is the block's byte offset from the tile start; rows past the
+// resource's range (the document end) read as zero.
+__device__ __forceinline__ void load_block4(uint4 (&r)[4], rsrc_t rsrc, uint32_t off0, uint32_t row_bytes) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int row = row0 + x;
-    r[x] = row < e ? *reinterpret_cast<const uint4*>(base + (size_t)row * rs + c8 * 8) : make_uint4(0, 0, 0, 0);
-  }
+  for (int x = 0; x < 4; ++x) r[x] = buf_load16(rsrc, off0 + x * row_bytes);
 }
 
 __device__ __forceinline__ void store_block4_rows(const uint4 (&r)[4], bf16* dst, int stride, int row0,
@@ -129,14 +127,8 @@ __device__ __forceinline__ void store_block4_transposed(const uint4 (&r)[4], bf1
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const int wi = c >> 1;
-    uint32_t lo, hi;
-    if (c & 1) {
-      lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-      hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-    } else {
-      lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-      hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-    }
+    const uint32_t lo = (c & 1) ? pack_hi16(w0[wi], w1[wi]) : pack_lo16(w0[wi], w1[wi]);
+    const uint32_t hi = (c & 1) ? pack_hi16(w2[wi], w3[wi]) : pack_lo16(w2[wi], w3[wi]);
     *reinterpret_cast<uint2*>(dst + (c8 * 8 + c) * stride + row0) = make_uint2(lo, hi);
   }
 }
@@ -189,12 +181,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
   const int qi = q0 + 32 * w + l32;
   const bool qvalid = qi < e;
 
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
   uint4 qreg[KK], doreg[KK];
+  {
+    const long long span = (long long)(e - q0) * row_bytes;
+    const rsrc_t qr = make_rsrc(a.q + base + (size_t)q0 * rs, span);
+    const rsrc_t dr = make_rsrc(a.dout + base + (size_t)q0 * rs, span);
+    const uint32_t off = (uint32_t)(32 * w + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const size_t off = base + (size_t)qi * rs + 16 * kk + 8 * half;
-    qreg[kk] = qvalid ? *reinterpret_cast<const uint4*>(a.q + off) : make_uint4(0, 0, 0, 0);
-    doreg[kk] = qvalid ? *reinterpret_cast<const uint4*>(a.dout + off) : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) {
+      qreg[kk] = buf_load16(qr, off + 32u * kk);
+      doreg[kk] = buf_load16(dr, off + 32u * kk);
+    }
   }
   const float lse2 = qvalid ? a.lse[(size_t)unit * a.N + qi] * kLog2e : 0.f;
   const float dlt = qvalid ? a.delta[(size_t)unit * a.N + qi] : 0.f;
@@ -208,16 +206,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[cb][i] = 0.f;
 
+  static_assert(BPT == 1, "one 4x8 block of K and of V per thread");
   uint4 kr[BPT][4], vr[BPT][4];
+  // this thread's block: keys 4*(tid % 16) .. +3, columns 8*(tid / 16) .. +7
+  const uint32_t blk_off = (uint32_t)(4 * (tid % (kDqBK / 4))) * row_bytes + (uint32_t)(tid / (kDqBK / 4)) * 16u;
   auto load = [&](int kt0) {
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int id = tid + j * kThreads;
-      if (id < BLOCKS) {
-        const int kg = id % (kDqBK / 4), cg = id / (kDqBK / 4);
-        load_block4(kr[j], a.k + base, rs, kt0 + 4 * kg, cg, e);
-        load_block4(vr[j], a.v + base, rs, kt0 + 4 * kg, cg, e);
-      }
+    if (tid < BLOCKS) {
+      const long long span = (long long)(e - kt0) * row_bytes;
+      load_block4(kr[0], make_rsrc(a.k + base + (size_t)kt0 * rs, span), blk_off, row_bytes);
+      load_block4(vr[0], make_rsrc(a.v + base + (size_t)kt0 * rs, span), blk_off, row_bytes);
     }
   };
   load(s);
@@ -255,6 +252,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
         }
       }
       const bool need_mask = (a.causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
+      if (need_mask) {
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (key >= e || (a.causal && key > qi)) sacc[blk][i] = -INFINITY;
+          }
+      }
       uint4 dsb[4];
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
@@ -264,11 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * mm + j;
-            float p = fast_exp2(sacc[blk][i] * a.sl2 - lse2);
-            if (need_mask) {
-              const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-              if (key >= e || (a.causal && key > qi)) p = 0.f;
-            }
+            const float p = fast_exp2(fmaf(sacc[blk][i], a.sl2, -lse2));
             ds[j] = p * (pacc[blk][i] - dlt);
           }
           dsb[blk * 2 + mm] = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
@@ -299,19 +301,19 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------- dkdv kernel
-constexpr int kKvBK = 128;  // keys per workgroup
-constexpr int kKvBQ = 32;   // queries per tile
+constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
+constexpr int kKvBQ = 64;   // queries per tile (two 32-query MFMA blocks)
 
 template <int D>
 struct KvSmem {
-  static constexpr int RS = D + 8;        // row-major Q / dO stride
-  static constexpr int TS = kKvBQ + 4;    // transposed Q^T / dO^T stride
+  static constexpr int RS = D + 8;        // row-major Q / dO stride (bf16)
+  static constexpr int TS = kKvBQ + 4;    // transposed Q^T / dO^T stride (bf16)
   static constexpr int Q_OFF = 0;
   static constexpr int DO_OFF = kKvBQ * RS;
   static constexpr int QT_OFF = 2 * kKvBQ * RS;
   static constexpr int DOT_OFF = QT_OFF + D * TS;
-  static constexpr int ELEMS = 2 * kKvBQ * RS + 2 * D * TS;  // bf16 elements
-  static constexpr int STAGE_BYTES = ELEMS * 2 + 2 * kKvBQ * 4;  // + lse2 and D
+  static constexpr int ELEMS = 2 * kKvBQ * RS + 2 * D * TS;      // bf16 elements
+  static constexpr int STAGE_BYTES = ELEMS * 2 + 2 * kKvBQ * 4;  // + lse (log2 units) and D
 };
 
 template <int D>
@@ -319,6 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
   using S = KvSmem<D>;
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int BLOCKS = (kKvBQ / 4) * (D / 8);  // 4x8 blocks of one Q (or dO) tile
+  constexpr int BPT = (BLOCKS + kThreads - 1) / kThreads;
   __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * S::STAGE_BYTES];
 
   const int per_level = a.ndoc * a.units;
@@ -338,13 +341,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int kj = kb0 + 32 * w + l32;
   const bool kvalid = kj < e;
+  const int wk0 = kb0 + 32 * w;  // first key of this wave
 
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
   uint4 kreg[KK], vreg[KK];
+  {
+    const long long span = (long long)(e - kb0) * row_bytes;
+    const rsrc_t kr = make_rsrc(a.k + base + (size_t)kb0 * rs, span);
+    const rsrc_t vr = make_rsrc(a.v + base + (size_t)kb0 * rs, span);
+    const uint32_t off = (uint32_t)(32 * w + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    const size_t off = base + (size_t)kj * rs + 16 * kk + 8 * half;
-    kreg[kk] = kvalid ? *reinterpret_cast<const uint4*>(a.k + off) : make_uint4(0, 0, 0, 0);
-    vreg[kk] = kvalid ? *reinterpret_cast<const uint4*>(a.v + off) : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) {
+      kreg[kk] = buf_load16(kr, off + 32u * kk);
+      vreg[kk] = buf_load16(vr, off + 32u * kk);
+    }
   }
 
   const int qstart = a.causal ? kb0 : s;
@@ -358,30 +368,45 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
 #pragma unroll
     for (int i = 0; i < 16; ++i) dkacc[cb][i] = dvacc[cb][i] = 0.f;
 
-  // staging: threads [0, 128) carry Q blocks, [128, 256) dO blocks; threads
-  // [0, 32) also the tile's lse (log2 units), [32, 64) its D.
-  const int which = tid >> 7, bid = tid & 127;
-  const bool has_block = bid < BLOCKS;
-  const int qg = bid % (kKvBQ / 4), cg = bid / (kKvBQ / 4);
-  const bf16* src = which ? a.dout + base : a.q + base;
-  uint4 r[4];
+  // staging: every thread carries one 4x8 block of Q and the same block of dO
+  // (BPT per thread); threads [0, 64) also the tile's lse (log2 units), [64, 128) its D.
+  uint4 rq[BPT][4], rd[BPT][4];
   float sv = 0.f;
   auto load = [&](int qt0) {
-    if (has_block) load_block4(r, src, rs, qt0 + 4 * qg, cg, e);
-    if (tid < 64) {
-      const int qq = qt0 + (tid & 31);
-      if (tid < 32) sv = qq < e ? lse_u[qq] * kLog2e : 0.f;
+    const long long span = (long long)(e - qt0) * row_bytes;
+    const rsrc_t qr = make_rsrc(a.q + base + (size_t)qt0 * rs, span);
+    const rsrc_t dr = make_rsrc(a.dout + base + (size_t)qt0 * rs, span);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int id = tid + j * kThreads;
+      if (id < BLOCKS) {
+        const int qg = id % (kKvBQ / 4), cg = id / (kKvBQ / 4);
+        const uint32_t off0 = (uint32_t)(4 * qg) * row_bytes + (uint32_t)cg * 16u;
+        load_block4(rq[j], qr, off0, row_bytes);
+        load_block4(rd[j], dr, off0, row_bytes);
+      }
+    }
+    if (tid < 2 * kKvBQ) {
+      const int qq = qt0 + (tid % kKvBQ);
+      if (tid < kKvBQ) sv = qq < e ? lse_u[qq] * kLog2e : 0.f;
       else sv = qq < e ? dl_u[qq] : 0.f;
     }
   };
   auto store = [&](uint8_t* stage) {
     bf16* sm = reinterpret_cast<bf16*>(stage);
     float* sf = reinterpret_cast<float*>(stage + S::ELEMS * 2);
-    if (has_block) {
-      store_block4_rows(r, sm + (which ? S::DO_OFF : S::Q_OFF), S::RS, 4 * qg, cg);
-      store_block4_transposed(r, sm + (which ? S::DOT_OFF : S::QT_OFF), S::TS, 4 * qg, cg);
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) {
+      const int id = tid + j * kThreads;
+      if (id < BLOCKS) {
+        const int qg = id % (kKvBQ / 4), cg = id / (kKvBQ / 4);
+        store_block4_rows(rq[j], sm + S::Q_OFF, S::RS, 4 * qg, cg);
+        store_block4_transposed(rq[j], sm + S::QT_OFF, S::TS, 4 * qg, cg);
+        store_block4_rows(rd[j], sm + S::DO_OFF, S::RS, 4 * qg, cg);
+        store_block4_transposed(rd[j], sm + S::DOT_OFF, S::TS, 4 * qg, cg);
+      }
     }
-    if (tid < 64) sf[tid] = sv;
+    if (tid < 2 * kKvBQ) sf[tid] = sv;
   };
 
   load(qstart);
@@ -396,40 +421,45 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
     const bool more = t + 1 < ntiles;
     if (more) load(qt0 + kKvBQ);
 
-    const bool wave_active = !a.causal || qt0 + kKvBQ - 1 >= kb0 + 32 * w;
-    if (wave_active) {
+    const bool need_mask = (a.causal && qt0 < kb0 + kKvBK - 1) || qt0 + kKvBQ > e || kb0 + kKvBK > e;
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      const int qb0 = qt0 + 32 * qb;
+      // causal: a 32-query block that ends before this wave's first key adds nothing
+      if (a.causal && qb0 + 31 < wk0) continue;
       f32x16 sacc, pacc;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int off = l32 * S::RS + 16 * kk + 8 * half;
+        const int off = (32 * qb + l32) * S::RS + 16 * kk + 8 * half;
         const uint4 qa = *reinterpret_cast<const uint4*>(sm + S::Q_OFF + off);
         const uint4 da = *reinterpret_cast<const uint4*>(sm + S::DO_OFF + off);
         sacc = mfma32(as_bf16x8(qa), as_bf16x8(kreg[kk]), sacc);
         pacc = mfma32(as_bf16x8(da), as_bf16x8(vreg[kk]), pacc);
       }
-      // lane = key kj; element i is query qt0 + 8*(i/4) + 4*half + (i%4)
-      const bool need_mask = (a.causal && qt0 < kb0 + kKvBK - 1) || qt0 + kKvBQ > e || kb0 + kKvBK > e;
+      // lane = key kj; element i is query qb0 + 8*(i/4) + 4*half + (i%4)
+      if (need_mask) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qq = qb0 + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (qq >= e || !kvalid || (a.causal && kj > qq)) sacc[i] = -INFINITY;
+        }
+      }
       uint4 pb[2], dsb[2];
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const float4 l4 = *reinterpret_cast<const float4*>(sf + 8 * gq + 4 * half);
-        const float4 d4 = *reinterpret_cast<const float4*>(sf + kKvBQ + 8 * gq + 4 * half);
+        const float4 l4 = *reinterpret_cast<const float4*>(sf + 32 * qb + 8 * gq + 4 * half);
+        const float4 d4 = *reinterpret_cast<const float4*>(sf + kKvBQ + 32 * qb + 8 * gq + 4 * half);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
         float p[4], ds[4];
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
-          const int i = 4 * gq + x;
-          p[x] = fast_exp2(sacc[i] * a.sl2 - lv[x]);
-          if (need_mask) {
-            const int qq = qt0 + 8 * gq + 4 * half + x;
-            if (qq >= e || !kvalid || (a.causal && kj > qq)) p[x] = 0.f;
-          }
-          ds[x] = p[x] * (pacc[i] - dv[x]);
+          p[x] = fast_exp2(fmaf(sacc[4 * gq + x], a.sl2, -lv[x]));
+          ds[x] = p[x] * (pacc[4 * gq + x] - dv[x]);
         }
-        // step mm = gq / 2 holds accumulator elements 8*mm .. 8*mm+7
+        // MFMA step mm = gq / 2 takes accumulator elements 8*mm .. 8*mm+7
         const int mm = gq >> 1;
         if ((gq & 1) == 0) {
           pb[mm].x = pack_bf16x2(p[0], p[1]);
@@ -445,8 +475,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
       }
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
-        const bf16* dotrow = sm + S::DOT_OFF + (cb * 32 + l32) * S::TS;
-        const bf16* qtrow = sm + S::QT_OFF + (cb * 32 + l32) * S::TS;
+        const bf16* dotrow = sm + S::DOT_OFF + (cb * 32 + l32) * S::TS + 32 * qb;
+        const bf16* qtrow = sm + S::QT_OFF + (cb * 32 + l32) * S::TS + 32 * qb;
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
           dvacc[cb] = mfma32(a_from_transposed(dotrow, 16 * mm, half), as_bf16x8(pb[mm]), dvacc[cb]);

@@ -16,8 +16,8 @@
 //     registers for the whole kernel. In the S^T accumulator layout a lane
 //     holds one query and 16 keys, so row max and row sum are in-register
 //     except for one exchange between the two half-waves.
-//   * Online softmax in the exp2 domain (log2(e)/sqrt(d) folded into one
-//     multiply). P^T is packed to bf16 straight from the accumulator and is
+//   * Online softmax in the exp2 domain (log2(e)/sqrt(d) folded into the
+//     exponent's FMA), with a lazily moved running max (see kRescaleSlack). P^T is packed to bf16 straight from the accumulator and is
 //     the B operand of O^T += V^T P^T, again a 32x32x16 MFMA, with V^T read
 //     from LDS. The MFMA k index is mapped to keys so that each lane's own
 //     P values form its B operand (no data movement between lanes). The O^T
@@ -26,7 +26,8 @@
 //   * K/V tiles of 64 keys are staged in LDS (K row-major, V transposed),
 //     double-buffered: the global loads of tile t+1 are issued before the
 //     math of tile t and written to the other buffer after it, one barrier
-//     per tile.
+//     per tile. Loads go through buffer resources ending at the document
+//     end (hardware zero-fill past it; per-thread offsets fixed per kernel).
 //   * Documents: a query tile never straddles a document; its keys run from
 //     the document start to the tile's last query (causal) or the document
 //     end. Only the tiles that cross the diagonal or the document end are
@@ -75,39 +76,42 @@ struct FwdArgs {
   float sl2;  // log2(e) / sqrt(d)
 };
 
-// Global -> register staging of one K/V tile (rows >= e are zero).
+// Global -> register staging of one K/V tile. Every load goes through a
+// buffer resource whose range ends at the document end, so rows past it read
+// as zero and the per-thread byte offsets are the same for every tile.
 template <int D>
 struct TileRegs {
-  static constexpr int KCH = kBK * D / 8 / kThreads;                 // 16-byte K chunks per thread
-  static constexpr int VBL = (kBK / 4) * (D / 8);                    // 4x8 V blocks per tile
-  static constexpr int VPT = (VBL + kThreads - 1) / kThreads;        // per thread
+  static constexpr int KCH = kBK * D / 8 / kThreads;           // 16-byte K chunks per thread
+  static constexpr int VBL = (kBK / 4) * (D / 8);              // 4-key x 8-column V blocks per tile
+  static constexpr int VPT = (VBL + kThreads - 1) / kThreads;  // V blocks per thread
   uint4 kr[KCH];
   uint4 vr[VPT][4];
 };
 
+// Per-thread byte offsets of the staging loads. Thread tid loads K chunks
+// id = tid + j*kThreads (key id/(D/8), 16-byte column id%(D/8)); since
+// kThreads is a multiple of D/8 these are k0 + j*kKeyStep rows apart. Its V
+// block (4 keys from 4*(tid % 16), 8 columns from 8*(tid / 16)) starts at v0.
 template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const bf16* kb, const bf16* vb, size_t rs,
-                                          int kt0, int e, int tid) {
-#pragma unroll
-  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
-    const int id = tid + j * kThreads;
-    const int key = id / (D / 8), c8 = id % (D / 8);
-    const int row = kt0 + key;
-    r.kr[j] = row < e ? *reinterpret_cast<const uint4*>(kb + (size_t)row * rs + c8 * 8) : make_uint4(0, 0, 0, 0);
+struct TileOffsets {
+  static constexpr int kKeyStep = kThreads / (D / 8);
+  uint32_t k0, v0;
+  __device__ TileOffsets(int tid, uint32_t row_bytes) {
+    k0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
+    v0 = (uint32_t)(4 * (tid % (kBK / 4))) * row_bytes + (uint32_t)(tid / (kBK / 4)) * 16u;
   }
+};
+
+template <int D>
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, const TileOffsets<D>& off, rsrc_t kr, rsrc_t vr,
+                                          uint32_t row_bytes, int tid) {
+  static_assert(TileRegs<D>::VPT == 1, "one V block per thread");
 #pragma unroll
-  for (int j = 0; j < TileRegs<D>::VPT; ++j) {
-    const int id = tid + j * kThreads;
-    if (id < TileRegs<D>::VBL) {
-      const int kg = id % (kBK / 4), cg = id / (kBK / 4);
+  for (int j = 0; j < TileRegs<D>::KCH; ++j)
+    r.kr[j] = buf_load16(kr, off.k0 + (uint32_t)(j * TileOffsets<D>::kKeyStep) * row_bytes);
+  if (tid < TileRegs<D>::VBL)
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int row = kt0 + 4 * kg + x;
-        r.vr[j][x] = row < e ? *reinterpret_cast<const uint4*>(vb + (size_t)row * rs + cg * 8)
-                             : make_uint4(0, 0, 0, 0);
-      }
-    }
-  }
+    for (int x = 0; x < 4; ++x) r.vr[0][x] = buf_load16(vr, off.v0 + x * row_bytes);
 }
 
 template <int D>
@@ -116,15 +120,14 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16*
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::KCH; ++j) {
     const int id = tid + j * kThreads;
-    const int key = id / (D / 8), c8 = id % (D / 8);
-    *reinterpret_cast<uint4*>(ks + key * S::KS + c8 * 8) = r.kr[j];
+    *reinterpret_cast<uint4*>(ks + (id / (D / 8)) * S::KS + (id % (D / 8)) * 8) = r.kr[j];
   }
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::VPT; ++j) {
     const int id = tid + j * kThreads;
     if (id < TileRegs<D>::VBL) {
       const int kg = id % (kBK / 4), cg = id / (kBK / 4);
-      // 4 keys x 8 columns -> 8 rows of V^T with 4 consecutive keys each.
+      // 4 keys x 8 columns -> 8 rows of V^T holding 4 consecutive keys each
       const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.vr[j][0]);
       const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.vr[j][1]);
       const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.vr[j][2]);
@@ -132,19 +135,20 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16*
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const int wi = c >> 1;
-        uint32_t lo, hi;
-        if (c & 1) {
-          lo = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-          hi = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-        } else {
-          lo = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-          hi = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-        }
+        const uint32_t lo = (c & 1) ? pack_hi16(w0[wi], w1[wi]) : pack_lo16(w0[wi], w1[wi]);
+        const uint32_t hi = (c & 1) ? pack_hi16(w2[wi], w3[wi]) : pack_lo16(w2[wi], w3[wi]);
         *reinterpret_cast<uint2*>(vs + (cg * 8 + c) * S::VS + kg * 4) = make_uint2(lo, hi);
       }
     }
   }
 }
+
+// Lazy rescale: the running max used in the exponentials only moves when a
+// row's new maximum exceeds it by more than 8 (log2 units). The O accumulator
+// is then rescaled rarely, and P = exp2(x - m) stays below 2^8, which fp32
+// sums and bf16 MFMA operands hold as exactly as values below 1; the final
+// normalisation uses the same m, so the result is unchanged.
+constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
@@ -180,12 +184,15 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int qi = q0 + 32 * w + l32;  // this lane's query
   const bool qvalid = qi < e;
 
-  // ---- Q^T operand, resident for the whole kernel
+  // ---- Q^T operand, resident for the whole kernel (rows past the document end read as zero)
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
   uint4 qreg[KK];
+  {
+    const rsrc_t qr = make_rsrc(qb + (size_t)q0 * rs, (long long)(e - q0) * row_bytes);
+    const uint32_t qoff = (uint32_t)(32 * w + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    qreg[kk] = qvalid ? *reinterpret_cast<const uint4*>(qb + (size_t)qi * rs + 16 * kk + 8 * half)
-                      : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) qreg[kk] = buf_load16(qr, qoff + 32u * kk);
+  }
 
   const int kend = a.causal ? min(e, q0 + kBQ) : e;
   const int ntiles = (kend - s + kBK - 1) / kBK;
@@ -197,8 +204,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
+  const TileOffsets<D> off(tid, row_bytes);
   TileRegs<D> tr;
-  load_tile<D>(tr, kb, vb, rs, s, e, tid);
+  auto rsrc_at = [&](const bf16* p, int kt0) {
+    return make_rsrc(p + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
+  };
+  load_tile<D>(tr, off, rsrc_at(kb, s), rsrc_at(vb, s), row_bytes, tid);
   store_tile<D>(tr, smem, smem + S::K_ELEMS, tid);
   __syncthreads();
 
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     const bf16* ks = smem + (t & 1) * S::STAGE;
     const bf16* vs = ks + S::K_ELEMS;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile<D>(tr, kb, vb, rs, kt0 + kBK, e, tid);
+    if (more) load_tile<D>(tr, off, rsrc_at(kb, kt0 + kBK), rsrc_at(vb, kt0 + kBK), row_bytes, tid);
 
     const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
     if (wave_active) {
@@ -223,30 +234,39 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           sacc[blk] = mfma32(as_bf16x8(av), as_bf16x8(qreg[kk]), sacc[blk]);
         }
       }
-      // scale to the log2 domain, mask where the tile crosses the diagonal or the document end
+      // mask where the tile crosses the diagonal or the document end (scale applied in the exponent)
       const bool need_mask = (a.causal && kt0 + kBK - 1 > q0) || kt0 + kBK > e;
       float mloc = -INFINITY;
+      if (need_mask) {
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = sacc[blk][i] * a.sl2;
-          if (need_mask) {
+          for (int i = 0; i < 16; ++i) {
+            float x = sacc[blk][i];
             const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
             if (key >= e || (a.causal && key > qi)) x = -INFINITY;
+            sacc[blk][i] = x;
+            mloc = fmaxf(mloc, x);
           }
-          sacc[blk][i] = x;
-          mloc = fmaxf(mloc, x);
-        }
-      mloc = fmaxf(mloc, swap_halves(mloc));
-      const float m_new = fmaxf(m_run, mloc);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
+      } else {
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
+        for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+          for (int i = 0; i < 16; ++i) {
+            mloc = fmaxf(mloc, sacc[blk][i]);
+          }
+      }
+      mloc = fmaxf(mloc, swap_halves(mloc)) * a.sl2;
+      if (__any(mloc > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, mloc);
+        const float alpha = fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+      }
 
       // P^T = exp2(x - m), packed to bf16 as the B operand of four 16-key MFMA steps
       uint4 pb[4];
@@ -257,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           float p[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(sacc[blk][8 * mm + j] - m_run);
+            p[j] = fast_exp2(fmaf(sacc[blk][8 * mm + j], a.sl2, -m_run));
             l_run += p[j];
           }
           pb[blk * 2 + mm] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),

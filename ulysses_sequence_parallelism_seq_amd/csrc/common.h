@@ -30,11 +30,33 @@ __device__ __forceinline__ uint4 make_bf16x8_bits(uint2 lo, uint2 hi) {
   return make_uint4(lo.x, lo.y, hi.x, hi.y);
 }
 
-// Round-to-nearest-even fp32 -> bf16 of two values, packed low|high.
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float float2_t;
+
+// Round-to-nearest-even fp32 -> bf16 of two values, packed low|high (one v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  bf16 a = (bf16)lo;
-  bf16 b = (bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  const float2_t f = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// Buffer resource over [base, base + bytes): loads at byte offsets >= bytes
+// return zero without touching memory (raw buffer, stride 0, range-checked
+// on the per-lane offset). Used to zero-fill rows past a document end.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, long long bytes) {
+  const int n = bytes <= 0 ? 0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
+}
+
+// 16-bit halves of two words: (hi.lo16 << 16 | lo.lo16) and (hi.hi16 << 16 | lo.hi16).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t lo, uint32_t hi) {
+  return __builtin_amdgcn_perm(hi, lo, 0x07060302u);
 }
 
 // Elements i0 .. i0+3 of an accumulator, times s, as four packed bf16.
@@ -76,8 +98,10 @@ inline int check_attn_args(int ndoc, int max_doc_len, const int* cu, int sp, int
     if (ndoc < 1 || max_doc_len < 1) return ULY_EINVAL;
     if (max_doc_len > N) return ULY_ESHAPE;
   }
-  // Token and element offsets are formed in 64 bits; launch sizes in 32.
+  // Token and element offsets are formed in 64 bits; launch sizes in 32;
+  // one (row, head) sequence must span < 2 GiB (32-bit buffer offsets).
   if ((long long)sp * B * Hl > (1LL << 24)) return ULY_ESHAPE;
+  if ((long long)N * Hl * d * (long long)elem_size(dtype) >= (1LL << 31)) return ULY_ESHAPE;
   return ULY_OK;
 }
 
