@@ -32,6 +32,9 @@ import torch
 
 import workloads
 import ulysses_sequence_parallelism_seq_amd as uly
+from ulysses_sequence_parallelism_seq_amd.traffic import read_traffic
+
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attn_bwd_long_traffic.txt")
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk/CU)
 PEAK_HBM_GBS = 8000.0
@@ -121,12 +124,15 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
         oracle.attn_bwd(q, k, v, do, None, True)
         return time.perf_counter() - t0
 
+    # cost grows as M^2: grow the prefix until a run takes a third of the target,
+    # then size the measured run to take about target_s
     M = 2048
     t = run(M)
-    # cost grows as M^2: pick the prefix that takes about target_s
-    M2 = int(M * (target_s / max(t, 1e-3)) ** 0.5) // 256 * 256
-    M2 = max(2048, min(M2, w.N))
-    if M2 != M:
+    while t < target_s / 3 and M < w.N:
+        M = min(2 * M, w.N)
+        t = run(M)
+    M2 = max(2048, min(int(M * (target_s / max(t, 1e-3)) ** 0.5) // 256 * 256, w.N))
+    if M2 > M:
         M, t = M2, run(M2)
     flops = 14 * w.d * (M * (M + 1) // 2)
     return {
@@ -198,6 +204,9 @@ def main():
     tensor_bytes = w.B * w.N * w.H * w.d * esize
     permute_gbs = 2 * tensor_bytes / (statistics.mean([avg["seq_to_head"], avg["head_to_seq"]]) * 1e-3) / 1e9
     bwd_tflops = 10 * w.d * pairs / (avg["attn_bwd"] * 1e-3) / 1e12
+    traffic = read_traffic(TRAFFIC_FILE) if args.workload == "long" else None
+    # compulsory bytes of one backward call: read q, k, v, o, dO, lse; write dq, dk, dv
+    min_bwd_bytes = 8 * w.sp * w.B * w.N * w.Hl * w.d * esize + w.sp * w.B * w.Hl * w.N * 4
     fwd_tflops = 4 * w.d * pairs / (avg["attn_fwd"] * 1e-3) / 1e12
 
     result = {
@@ -235,7 +244,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic["bytes"]),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "compulsory_bytes": min_bwd_bytes,
+            "flops_per_launch": 10 * w.d * pairs,
         },
         "cpu_baseline": None,
     }

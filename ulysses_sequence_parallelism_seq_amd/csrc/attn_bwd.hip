@@ -14,15 +14,18 @@
 // results are bit-reproducible):
 //   * dq kernel, query-stationary: a workgroup owns 128 queries (32 per
 //     wave, Q and dO resident in registers as MFMA B operands) and walks the
-//     64-key K/V tiles of its document. Per tile: S^T = K Q^T and
+//     64-key K/V tiles of its document (double-buffered in LDS). Per tile: S^T = K Q^T and
 //     dP^T = V dO^T (lane = query, so lse_i and D_i are per-lane scalars),
-//     dS^T in registers, then dQ^T += K^T dS^T with K^T staged in LDS.
-//   * dkdv kernel, key-stationary: a workgroup owns 128 keys (32 per wave, K
-//     and V resident as B operands) and walks 32-query tiles from its first
-//     key (causal) to the document end. Per tile: S = Q K^T and dP = dO V^T
-//     (lane = key), then dV^T += dO^T P and dK^T += Q^T dS with Q^T and
-//     dO^T staged in LDS; the accumulators hold one key per lane, so the
-//     final stores are 4 consecutive columns per lane.
+//     dS^T in registers, then dQ^T += K^T dS^T (K^T read from the row-major
+//     K tile with gfx950's transposing LDS reads).
+//   * dkdv kernel, key-stationary: a workgroup of 8 waves owns 128 keys (K
+//     and V resident as B operands, each 32-key group shared by two waves)
+//     and walks 64-query tiles (Q, dO, lse, D double-buffered in LDS) from the
+//     document end down to its first key (causal). Per tile: S = Q K^T and dP = dO V^T
+//     (lane = key), then dV^T += dO^T P and dK^T += Q^T dS with the A
+//     operands read transposed from the row-major Q and dO tiles; the
+//     accumulators hold one key per lane, so the final stores are 4
+//     consecutive columns per lane.
 // The MFMA k index of a 16-wide step maps to tokens the same way as in the
 // forward kernel, so P and dS feed the MFMA straight from the accumulators.
 
@@ -103,65 +106,50 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
 }
 
 // ----------------------------------------------------------- shared tile staging
-// A 4-token x 8-column block of a [token][d] tensor, loaded as four 16-byte
-// rows; written to LDS row-major and/or transposed ([column][token]).
-// off0 is the block's byte offset from the tile start; rows past the
-// resource's range (the document end) read as zero.
-__device__ __forceinline__ void load_block4(uint4 (&r)[4], rsrc_t rsrc, uint32_t off0, uint32_t row_bytes) {
-#pragma unroll
-  for (int x = 0; x < 4; ++x) r[x] = buf_load16(rsrc, off0 + x * row_bytes);
-}
+// A tile of kRows tokens of two [token][d] tensors, staged global -> registers
+// -> LDS (RowTile layout) by kNT threads. Thread tid moves the 16-byte chunks
+// id = tid + j*kNT (token id/(D/8), column chunk id%(D/8)). Loads go
+// through buffer resources ending at the document end: rows past it read as
+// zero and the per-thread offsets are the same for every tile.
+template <int D, int kRows, int kNT = kThreads>
+struct PairTile {
+  using L = RowTile<D>;
+  static constexpr int RS = L::RS;                  // LDS row stride (bf16)
+  static constexpr int CH = kRows * D / 8 / kNT;    // chunks per thread per tensor
+  static constexpr int kRowStep = kNT / (D / 8);    // tokens between a thread's chunks
+  uint4 a[CH];
+  uint4 b[CH];
 
-__device__ __forceinline__ void store_block4_rows(const uint4 (&r)[4], bf16* dst, int stride, int row0,
-                                                  int c8) {
+  __device__ __forceinline__ void load(rsrc_t ra, rsrc_t rb, uint32_t off0, uint32_t row_bytes) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) *reinterpret_cast<uint4*>(dst + (row0 + x) * stride + c8 * 8) = r[x];
-}
-
-__device__ __forceinline__ void store_block4_transposed(const uint4 (&r)[4], bf16* dst, int stride,
-                                                        int row0, int c8) {
-  const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r[0]);
-  const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r[1]);
-  const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r[2]);
-  const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r[3]);
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const int wi = c >> 1;
-    const uint32_t lo = (c & 1) ? pack_hi16(w0[wi], w1[wi]) : pack_lo16(w0[wi], w1[wi]);
-    const uint32_t hi = (c & 1) ? pack_hi16(w2[wi], w3[wi]) : pack_lo16(w2[wi], w3[wi]);
-    *reinterpret_cast<uint2*>(dst + (c8 * 8 + c) * stride + row0) = make_uint2(lo, hi);
+    for (int j = 0; j < CH; ++j) {
+      const uint32_t off = off0 + (uint32_t)(j * kRowStep) * row_bytes;
+      a[j] = buf_load16(ra, off);
+      b[j] = buf_load16(rb, off);
+    }
   }
-}
-
-// The MFMA A operand of a 16-token step from a transposed LDS row: tokens
-// off + 4*half + (0..3) and off + 8 + 4*half + (0..3).
-__device__ __forceinline__ bf16x8 a_from_transposed(const bf16* row, int off, int half) {
-  const uint2 lo = *reinterpret_cast<const uint2*>(row + off + 4 * half);
-  const uint2 hi = *reinterpret_cast<const uint2*>(row + off + 8 + 4 * half);
-  return as_bf16x8(make_bf16x8_bits(lo, hi));
-}
+  __device__ __forceinline__ void store(bf16* sa, bf16* sb, int tid) const {
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int at = L::off(tid / (D / 8) + j * kRowStep, (tid % (D / 8)) * 8);
+      *reinterpret_cast<uint4*>(sa + at) = a[j];
+      *reinterpret_cast<uint4*>(sb + at) = b[j];
+    }
+  }
+};
 
 // --------------------------------------------------------------------- dq kernel
-constexpr int kDqBQ = 128;  // queries per workgroup
+constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kDqBK = 64;   // keys per tile
 
 template <int D>
-struct DqSmem {
-  static constexpr int KS = D + 8;
-  static constexpr int TS = kDqBK + 4;
-  static constexpr int K_OFF = 0;
-  static constexpr int V_OFF = kDqBK * KS;
-  static constexpr int KT_OFF = 2 * kDqBK * KS;
-  static constexpr int ELEMS = 2 * kDqBK * KS + D * TS;
-};
-
-template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
-  using S = DqSmem<D>;
+  using T = PairTile<D, kDqBK>;
+  constexpr int RS = T::RS;
   constexpr int KK = D / 16, CB = D / 32;
-  constexpr int BLOCKS = (kDqBK / 4) * (D / 8);  // 4x8 blocks per K (or V) tile
-  constexpr int BPT = (BLOCKS + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) bf16 smem[S::ELEMS];
+  constexpr int TILE = kDqBK * RS;   // bf16 elements of one staged tensor
+  constexpr int STAGE = 2 * TILE;    // K then V
+  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
   const int per_level = a.ndoc * a.units;
   const int lvl = blockIdx.x / per_level;
@@ -171,17 +159,18 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
   int s, e;
   doc_range(a, doc, s, e);
   const int q0 = s + (a.nslots - 1 - lvl) * kDqBQ;
-  if (q0 >= e) return;
+  if (q0 >= e) return;  // the whole workgroup leaves before any barrier
 
   const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
   const size_t rs = (size_t)a.Hl * D;
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
   const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int qi = q0 + 32 * w + l32;
   const bool qvalid = qi < e;
 
-  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  // Q^T and dO^T as resident B operands (rows past the document end read as zero)
   uint4 qreg[KK], doreg[KK];
   {
     const long long span = (long long)(e - q0) * row_bytes;
@@ -206,86 +195,72 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[cb][i] = 0.f;
 
-  static_assert(BPT == 1, "one 4x8 block of K and of V per thread");
-  uint4 kr[BPT][4], vr[BPT][4];
-  // this thread's block: keys 4*(tid % 16) .. +3, columns 8*(tid / 16) .. +7
-  const uint32_t blk_off = (uint32_t)(4 * (tid % (kDqBK / 4))) * row_bytes + (uint32_t)(tid / (kDqBK / 4)) * 16u;
-  auto load = [&](int kt0) {
-    if (tid < BLOCKS) {
-      const long long span = (long long)(e - kt0) * row_bytes;
-      load_block4(kr[0], make_rsrc(a.k + base + (size_t)kt0 * rs, span), blk_off, row_bytes);
-      load_block4(vr[0], make_rsrc(a.v + base + (size_t)kt0 * rs, span), blk_off, row_bytes);
-    }
+  const uint32_t off0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
+  auto rsrc_at = [&](const bf16* p, int kt0) {
+    return make_rsrc(p + base + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
   };
-  load(s);
+  T tile;
+  tile.load(rsrc_at(a.k, s), rsrc_at(a.v, s), off0, row_bytes);
+  tile.store(smem, smem + TILE, tid);
+  __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
     const int kt0 = s + t * kDqBK;
-    __syncthreads();  // every wave is done with the previous tile
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int id = tid + j * kThreads;
-      if (id < BLOCKS) {
-        const int kg = id % (kDqBK / 4), cg = id / (kDqBK / 4);
-        store_block4_rows(kr[j], smem + S::K_OFF, S::KS, 4 * kg, cg);
-        store_block4_rows(vr[j], smem + S::V_OFF, S::KS, 4 * kg, cg);
-        store_block4_transposed(kr[j], smem + S::KT_OFF, S::TS, 4 * kg, cg);
-      }
-    }
-    __syncthreads();
-    if (t + 1 < ntiles) load(kt0 + kDqBK);
+    const bf16* ks = smem + (t & 1) * STAGE;
+    const bf16* vs = ks + TILE;
+    const bool more = t + 1 < ntiles;
+    if (more) tile.load(rsrc_at(a.k, kt0 + kDqBK), rsrc_at(a.v, kt0 + kDqBK), off0, row_bytes);
 
-    const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
-    if (wave_active) {
-      f32x16 sacc[2], pacc[2];
+    if (!a.causal || kt0 <= q0 + 32 * w + 31) {
+      const bool need_mask = (a.causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
+      // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (lane = query,
+      // element i is key kt0 + blk*32 + 8*(i/4) + 4*half + (i%4)), dS^T, then
+      // dQ^T += K^T dS^T with K^T read from the K tile by transposing reads
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
+        f32x16 sacc, pacc;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[blk][i] = pacc[blk][i] = 0.f;
+        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const int off = (blk * 32 + l32) * S::KS + 16 * kk + 8 * half;
-          const uint4 ka = *reinterpret_cast<const uint4*>(smem + S::K_OFF + off);
-          const uint4 va = *reinterpret_cast<const uint4*>(smem + S::V_OFF + off);
-          sacc[blk] = mfma32(as_bf16x8(ka), as_bf16x8(qreg[kk]), sacc[blk]);
-          pacc[blk] = mfma32(as_bf16x8(va), as_bf16x8(doreg[kk]), pacc[blk]);
+          const int off = T::L::off(blk * 32 + l32, 16 * kk + 8 * half);
+          const uint4 ka = *reinterpret_cast<const uint4*>(ks + off);
+          const uint4 va = *reinterpret_cast<const uint4*>(vs + off);
+          sacc = mfma32(as_bf16x8(ka), as_bf16x8(qreg[kk]), sacc);
+          pacc = mfma32(as_bf16x8(va), as_bf16x8(doreg[kk]), pacc);
         }
-      }
-      const bool need_mask = (a.causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
-      if (need_mask) {
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= e || (a.causal && key > qi)) sacc[blk][i] = -INFINITY;
+            if (key >= e || (a.causal && key > qi)) sacc[i] = -INFINITY;
           }
-      }
-      uint4 dsb[4];
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+        }
+        uint4 dsb[2];
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
           float ds[8];
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * mm + j;
-            const float p = fast_exp2(fmaf(sacc[blk][i], a.sl2, -lse2));
-            ds[j] = p * (pacc[blk][i] - dlt);
+            ds[j] = fast_exp2(fmaf(sacc[i], a.sl2, -lse2)) * (pacc[i] - dlt);
           }
-          dsb[blk * 2 + mm] = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]),
-                                         pack_bf16x2(ds[4], ds[5]), pack_bf16x2(ds[6], ds[7]));
+          dsb[mm] = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                               pack_bf16x2(ds[6], ds[7]));
         }
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const bf16* ktrow = smem + S::KT_OFF + (cb * 32 + l32) * S::TS;
+        for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int koff = (st >> 1) * 32 + (st & 1) * 16;
-          dqacc[cb] = mfma32(a_from_transposed(ktrow, koff, half), as_bf16x8(dsb[st]), dqacc[cb]);
-        }
+          for (int mm = 0; mm < 2; ++mm)
+            dqacc[cb] = mfma32(a_from_rows<D>(ks, 32 * blk + 16 * mm, 32 * cb, lane), as_bf16x8(dsb[mm]), dqacc[cb]);
       }
     }
+
+    if (more) {
+      bf16* nk = smem + ((t + 1) & 1) * STAGE;
+      tile.store(nk, nk + TILE, tid);
+    }
+    __syncthreads();
   }
 
   if (qvalid) {
@@ -293,36 +268,32 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int c = cb * 32 + 8 * gq + 4 * half;
-        *reinterpret_cast<uint2*>(out + c) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
-      }
+      for (int gq = 0; gq < 4; ++gq)
+        *reinterpret_cast<uint2*>(out + cb * 32 + 8 * gq + 4 * half) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
   }
 }
 
 // ------------------------------------------------------------------- dkdv kernel
-constexpr int kKvBK = 128;  // keys per workgroup (32 per wave)
-constexpr int kKvBQ = 64;   // queries per tile (two 32-query MFMA blocks)
+// 8 waves, 128 keys per workgroup. Waves w and w + 4 share the 32 keys
+// kb0 + 32*(w % 4): each computes S, dP, P and dS for one of the tile's two
+// 32-query blocks (block w / 4), hands its packed P and dS to the other wave
+// through LDS, and accumulates dK and dV for one half of the head dimension
+// (columns [w/4 * D/2, w/4 * D/2 + D/2)) over both blocks. No MFMA is done
+// twice, and with half the accumulators per wave two waves fit on a SIMD.
+constexpr int kKvBK = 128;      // keys per workgroup
+constexpr int kKvBQ = 64;       // queries per tile (two 32-query blocks)
+constexpr int kKvThreads = 512; // 8 waves
 
 template <int D>
-struct KvSmem {
-  static constexpr int RS = D + 8;        // row-major Q / dO stride (bf16)
-  static constexpr int TS = kKvBQ + 4;    // transposed Q^T / dO^T stride (bf16)
-  static constexpr int Q_OFF = 0;
-  static constexpr int DO_OFF = kKvBQ * RS;
-  static constexpr int QT_OFF = 2 * kKvBQ * RS;
-  static constexpr int DOT_OFF = QT_OFF + D * TS;
-  static constexpr int ELEMS = 2 * kKvBQ * RS + 2 * D * TS;      // bf16 elements
-  static constexpr int STAGE_BYTES = ELEMS * 2 + 2 * kKvBQ * 4;  // + lse (log2 units) and D
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) {
-  using S = KvSmem<D>;
-  constexpr int KK = D / 16, CB = D / 32;
-  constexpr int BLOCKS = (kKvBQ / 4) * (D / 8);  // 4x8 blocks of one Q (or dO) tile
-  constexpr int BPT = (BLOCKS + kThreads - 1) / kThreads;
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * S::STAGE_BYTES];
+__global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) {
+  using T = PairTile<D, kKvBQ, kKvThreads>;
+  constexpr int KK = D / 16;
+  constexpr int CBH = D / 64;                 // 32-column blocks per wave (half of D / 32)
+  constexpr int TILE = kKvBQ * T::RS;         // bf16 elements of one staged tensor
+  constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * kKvBQ * 4;  // Q, dO, then lse (log2 units) and D
+  constexpr int XCH_BYTES = 8 * 4 * 64 * 16;  // per wave: P and dS as 4 x 16 bytes per lane
+  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * STAGE_BYTES + XCH_BYTES];
+  uint4* xch = reinterpret_cast<uint4*>(smem_raw + 2 * STAGE_BYTES);
 
   const int per_level = a.ndoc * a.units;
   const int lvl = blockIdx.x / per_level;
@@ -332,24 +303,24 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
   int s, e;
   doc_range(a, doc, s, e);
   const int kb0 = s + lvl * kKvBK;  // causal: low key blocks have the most queries, so they go first
-  if (kb0 >= e) return;
+  if (kb0 >= e) return;             // the whole workgroup leaves before any barrier
 
   const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
   const size_t rs = (size_t)a.Hl * D;
+  const uint32_t row_bytes = (uint32_t)rs * 2u;
   const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const int kj = kb0 + 32 * w + l32;
-  const bool kvalid = kj < e;
-  const int wk0 = kb0 + 32 * w;  // first key of this wave
+  const int kgrp = w & 3, role = w >> 2;  // key group; query block and column half of this wave
+  const int kj = kb0 + 32 * kgrp + l32;
 
-  const uint32_t row_bytes = (uint32_t)rs * 2u;
+  // K^T and V^T of the wave's 32 keys as resident B operands (zero past the document end)
   uint4 kreg[KK], vreg[KK];
   {
     const long long span = (long long)(e - kb0) * row_bytes;
     const rsrc_t kr = make_rsrc(a.k + base + (size_t)kb0 * rs, span);
     const rsrc_t vr = make_rsrc(a.v + base + (size_t)kb0 * rs, span);
-    const uint32_t off = (uint32_t)(32 * w + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
+    const uint32_t off = (uint32_t)(32 * kgrp + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       kreg[kk] = buf_load16(kr, off + 32u * kk);
@@ -362,30 +333,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
   const float* lse_u = a.lse + (size_t)unit * a.N;
   const float* dl_u = a.delta + (size_t)unit * a.N;
 
-  f32x16 dkacc[CB], dvacc[CB];
+  f32x16 dkacc[CBH], dvacc[CBH];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
+  for (int c = 0; c < CBH; ++c)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) dkacc[cb][i] = dvacc[cb][i] = 0.f;
+    for (int i = 0; i < 16; ++i) dkacc[c][i] = dvacc[c][i] = 0.f;
 
-  // staging: every thread carries one 4x8 block of Q and the same block of dO
-  // (BPT per thread); threads [0, 64) also the tile's lse (log2 units), [64, 128) its D.
-  uint4 rq[BPT][4], rd[BPT][4];
+  // staging: Q and dO chunks; threads [0, 64) also carry the tile's lse (log2
+  // units), threads [64, 128) its D
+  const uint32_t off0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
+  T tile;
   float sv = 0.f;
   auto load = [&](int qt0) {
     const long long span = (long long)(e - qt0) * row_bytes;
-    const rsrc_t qr = make_rsrc(a.q + base + (size_t)qt0 * rs, span);
-    const rsrc_t dr = make_rsrc(a.dout + base + (size_t)qt0 * rs, span);
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int id = tid + j * kThreads;
-      if (id < BLOCKS) {
-        const int qg = id % (kKvBQ / 4), cg = id / (kKvBQ / 4);
-        const uint32_t off0 = (uint32_t)(4 * qg) * row_bytes + (uint32_t)cg * 16u;
-        load_block4(rq[j], qr, off0, row_bytes);
-        load_block4(rd[j], dr, off0, row_bytes);
-      }
-    }
+    tile.load(make_rsrc(a.q + base + (size_t)qt0 * rs, span), make_rsrc(a.dout + base + (size_t)qt0 * rs, span),
+              off0, row_bytes);
     if (tid < 2 * kKvBQ) {
       const int qq = qt0 + (tid % kKvBQ);
       if (tid < kKvBQ) sv = qq < e ? lse_u[qq] * kLog2e : 0.f;
@@ -394,110 +356,111 @@ __global__ __launch_bounds__(kThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) 
   };
   auto store = [&](uint8_t* stage) {
     bf16* sm = reinterpret_cast<bf16*>(stage);
-    float* sf = reinterpret_cast<float*>(stage + S::ELEMS * 2);
-#pragma unroll
-    for (int j = 0; j < BPT; ++j) {
-      const int id = tid + j * kThreads;
-      if (id < BLOCKS) {
-        const int qg = id % (kKvBQ / 4), cg = id / (kKvBQ / 4);
-        store_block4_rows(rq[j], sm + S::Q_OFF, S::RS, 4 * qg, cg);
-        store_block4_transposed(rq[j], sm + S::QT_OFF, S::TS, 4 * qg, cg);
-        store_block4_rows(rd[j], sm + S::DO_OFF, S::RS, 4 * qg, cg);
-        store_block4_transposed(rd[j], sm + S::DOT_OFF, S::TS, 4 * qg, cg);
-      }
-    }
-    if (tid < 2 * kKvBQ) sf[tid] = sv;
+    tile.store(sm, sm + TILE, tid);
+    if (tid < 2 * kKvBQ) reinterpret_cast<float*>(stage + 2 * TILE * 2)[tid] = sv;
   };
 
-  load(qstart);
+  // Query tiles are walked from the document end down to the first one this
+  // block needs: every workgroup of a head then reads the same Q/dO tile at
+  // about the same time, so the XCD's L2 serves them all.
+  const int qlast = qstart + (ntiles - 1) * kKvBQ;
+  load(qlast);
   store(smem_raw);
   __syncthreads();
 
   for (int t = 0; t < ntiles; ++t) {
-    const int qt0 = qstart + t * kKvBQ;
-    const uint8_t* stage = smem_raw + (t & 1) * S::STAGE_BYTES;
-    const bf16* sm = reinterpret_cast<const bf16*>(stage);
-    const float* sf = reinterpret_cast<const float*>(stage + S::ELEMS * 2);
+    const int qt0 = qlast - t * kKvBQ;
+    const uint8_t* stage = smem_raw + (t & 1) * STAGE_BYTES;
+    const bf16* qs = reinterpret_cast<const bf16*>(stage);
+    const bf16* dos = qs + TILE;
+    const float* sf = reinterpret_cast<const float*>(stage + 2 * TILE * 2);
     const bool more = t + 1 < ntiles;
-    if (more) load(qt0 + kKvBQ);
+    if (more) load(qt0 - kKvBQ);
 
+    // ---- this wave's query block: S = Q K^T, dP = dO V^T (lane = key kj,
+    // element i is query qb0 + 8*(i/4) + 4*half + (i%4)), then P and dS
+    const int qb0 = qt0 + 32 * role;
+    f32x16 sacc, pacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int off = RowTile<D>::off(32 * role + l32, 16 * kk + 8 * half);
+      const uint4 qa = *reinterpret_cast<const uint4*>(qs + off);
+      const uint4 da = *reinterpret_cast<const uint4*>(dos + off);
+      sacc = mfma32(as_bf16x8(qa), as_bf16x8(kreg[kk]), sacc);
+      pacc = mfma32(as_bf16x8(da), as_bf16x8(vreg[kk]), pacc);
+    }
+    // tiles that cross the diagonal or a document end are masked element by element
     const bool need_mask = (a.causal && qt0 < kb0 + kKvBK - 1) || qt0 + kKvBQ > e || kb0 + kKvBK > e;
+    float p[16], ds[16];
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      const float4 l4 = *reinterpret_cast<const float4*>(sf + 32 * role + 8 * gq + 4 * half);
+      const float4 d4 = *reinterpret_cast<const float4*>(sf + kKvBQ + 32 * role + 8 * gq + 4 * half);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        const int i = 4 * gq + x;
+        p[i] = fast_exp2(fmaf(sacc[i], a.sl2, -lv[x]));
+        ds[i] = pacc[i] - dv[x];
+      }
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qq = qb0 + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (qq >= e || kj >= e || (a.causal && kj > qq)) p[i] = 0.f;
+      }
+    }
+    // P then dS, each as two MFMA steps (accumulator elements 8*mm .. 8*mm+7),
+    // published for the partner wave (and read back by this one below)
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      const int b = 8 * mm;
+      xch[(w * 4 + mm) * 64 + lane] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
+                                                 pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
+      xch[(w * 4 + 2 + mm) * 64 + lane] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
+                                                     pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
+                                                     pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
+                                                     pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
+    }
+    __syncthreads();  // both blocks' P and dS are visible
+
+    // ---- dV^T += dO^T P and dK^T += Q^T dS over both query blocks, for this
+    // wave's half of the columns; A operands by transposing reads of dO and Q
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      const int qb0 = qt0 + 32 * qb;
-      // causal: a 32-query block that ends before this wave's first key adds nothing
-      if (a.causal && qb0 + 31 < wk0) continue;
-      f32x16 sacc, pacc;
+      const int owner = kgrp + 4 * qb;  // the wave that computed block qb for these keys
+      uint4 opnd[4];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+      for (int j = 0; j < 4; ++j) opnd[j] = xch[(owner * 4 + j) * 64 + lane];
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int off = (32 * qb + l32) * S::RS + 16 * kk + 8 * half;
-        const uint4 qa = *reinterpret_cast<const uint4*>(sm + S::Q_OFF + off);
-        const uint4 da = *reinterpret_cast<const uint4*>(sm + S::DO_OFF + off);
-        sacc = mfma32(as_bf16x8(qa), as_bf16x8(kreg[kk]), sacc);
-        pacc = mfma32(as_bf16x8(da), as_bf16x8(vreg[kk]), pacc);
-      }
-      // lane = key kj; element i is query qb0 + 8*(i/4) + 4*half + (i%4)
-      if (need_mask) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qq = qb0 + 8 * (i >> 2) + 4 * half + (i & 3);
-          if (qq >= e || !kvalid || (a.causal && kj > qq)) sacc[i] = -INFINITY;
-        }
-      }
-      uint4 pb[2], dsb[2];
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const float4 l4 = *reinterpret_cast<const float4*>(sf + 32 * qb + 8 * gq + 4 * half);
-        const float4 d4 = *reinterpret_cast<const float4*>(sf + kKvBQ + 32 * qb + 8 * gq + 4 * half);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-        float p[4], ds[4];
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          p[x] = fast_exp2(fmaf(sacc[4 * gq + x], a.sl2, -lv[x]));
-          ds[x] = p[x] * (pacc[4 * gq + x] - dv[x]);
-        }
-        // MFMA step mm = gq / 2 takes accumulator elements 8*mm .. 8*mm+7
-        const int mm = gq >> 1;
-        if ((gq & 1) == 0) {
-          pb[mm].x = pack_bf16x2(p[0], p[1]);
-          pb[mm].y = pack_bf16x2(p[2], p[3]);
-          dsb[mm].x = pack_bf16x2(ds[0], ds[1]);
-          dsb[mm].y = pack_bf16x2(ds[2], ds[3]);
-        } else {
-          pb[mm].z = pack_bf16x2(p[0], p[1]);
-          pb[mm].w = pack_bf16x2(p[2], p[3]);
-          dsb[mm].z = pack_bf16x2(ds[0], ds[1]);
-          dsb[mm].w = pack_bf16x2(ds[2], ds[3]);
-        }
-      }
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const bf16* dotrow = sm + S::DOT_OFF + (cb * 32 + l32) * S::TS + 32 * qb;
-        const bf16* qtrow = sm + S::QT_OFF + (cb * 32 + l32) * S::TS + 32 * qb;
+      for (int c = 0; c < CBH; ++c) {
+        const int c0 = 32 * (role * CBH + c);
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          dvacc[cb] = mfma32(a_from_transposed(dotrow, 16 * mm, half), as_bf16x8(pb[mm]), dvacc[cb]);
-          dkacc[cb] = mfma32(a_from_transposed(qtrow, 16 * mm, half), as_bf16x8(dsb[mm]), dkacc[cb]);
+          dvacc[c] = mfma32(a_from_rows<D>(dos, 32 * qb + 16 * mm, c0, lane), as_bf16x8(opnd[mm]), dvacc[c]);
+          dkacc[c] = mfma32(a_from_rows<D>(qs, 32 * qb + 16 * mm, c0, lane), as_bf16x8(opnd[2 + mm]), dkacc[c]);
         }
       }
     }
-    if (more) store(smem_raw + ((t + 1) & 1) * S::STAGE_BYTES);
+
+    if (more) store(smem_raw + ((t + 1) & 1) * STAGE_BYTES);
     __syncthreads();
   }
 
-  if (kvalid) {
+  if (kj < e) {
     bf16* ko = a.dk + base + (size_t)kj * rs;
     bf16* vo = a.dv + base + (size_t)kj * rs;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int c = 0; c < CBH; ++c)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int c = cb * 32 + 8 * gq + 4 * half;
-        *reinterpret_cast<uint2*>(ko + c) = pack4_scaled(dkacc[cb], 4 * gq, a.scale);
-        *reinterpret_cast<uint2*>(vo + c) = pack4_scaled(dvacc[cb], 4 * gq, 1.f);
+        const int col = 32 * (role * CBH + c) + 8 * gq + 4 * half;
+        *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[c], 4 * gq, a.scale);
+        *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[c], 4 * gq, 1.f);
       }
   }
 }
@@ -547,12 +510,12 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   if (g.d == 64) {
     hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
                        delta, g.N, g.Hl, rows);
-    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<64>, dim3((unsigned)kvblocks), dim3(kThreads), 0, st, akv);
+    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<64>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL(attn_dq_bf16_kernel<64>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, aq);
   } else {
     hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
                        delta, g.N, g.Hl, rows);
-    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<128>, dim3((unsigned)kvblocks), dim3(kThreads), 0, st, akv);
+    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<128>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL(attn_dq_bf16_kernel<128>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, aq);
   }
   return launch_status();

@@ -18,12 +18,14 @@
 //     except for one exchange between the two half-waves.
 //   * Online softmax in the exp2 domain (log2(e)/sqrt(d) folded into the
 //     exponent's FMA), with a lazily moved running max (see kRescaleSlack). P^T is packed to bf16 straight from the accumulator and is
-//     the B operand of O^T += V^T P^T, again a 32x32x16 MFMA, with V^T read
-//     from LDS. The MFMA k index is mapped to keys so that each lane's own
-//     P values form its B operand (no data movement between lanes). The O^T
+//     the B operand of O^T += V^T P^T, again a 32x32x16 MFMA, whose A
+//     operand V^T comes from the row-major V tile through gfx950's
+//     transposing LDS reads. The MFMA k index is mapped to keys so that each
+//     lane's own P values form its B operand (no data movement between
+//     lanes). The O^T
 //     accumulator has one query per lane, so the rescale by the running-max
 //     correction is a per-lane scalar.
-//   * K/V tiles of 64 keys are staged in LDS (K row-major, V transposed),
+//   * K/V tiles of 64 keys are staged in LDS (both row-major, padded rows),
 //     double-buffered: the global loads of tile t+1 are issued before the
 //     math of tile t and written to the other buffer after it, one barrier
 //     per tile. Loads go through buffer resources ending at the document
@@ -52,12 +54,10 @@ constexpr int kThreads = 256;
 
 template <int D>
 struct FwdSmem {
-  static constexpr int KS = D + 8;    // K row stride (bf16): conflict-free 16-byte reads
-  static constexpr int VS = kBK + 4;  // V^T row stride (bf16): conflict-free 8-byte reads
-  static constexpr int K_ELEMS = kBK * KS;
-  static constexpr int V_ELEMS = D * VS;
+  using L = RowTile<D>;  // K and V tiles, row-major (swizzled for d = 128)
+  static constexpr int K_ELEMS = kBK * L::RS;
+  static constexpr int V_ELEMS = kBK * L::RS;
   static constexpr int STAGE = K_ELEMS + V_ELEMS;
-  static constexpr int BYTES = 2 * STAGE * 2;
 };
 
 struct FwdArgs {
@@ -76,70 +76,38 @@ struct FwdArgs {
   float sl2;  // log2(e) / sqrt(d)
 };
 
-// Global -> register staging of one K/V tile. Every load goes through a
-// buffer resource whose range ends at the document end, so rows past it read
-// as zero and the per-thread byte offsets are the same for every tile.
+// Global -> register staging of one K/V tile: thread tid moves the 16-byte
+// chunks id = tid + j*kThreads (token id/(D/8), column chunk id%(D/8)) of K
+// and of V. Loads go through buffer resources whose range ends at the
+// document end, so rows past it read as zero and the per-thread offsets are
+// the same for every tile.
 template <int D>
 struct TileRegs {
-  static constexpr int KCH = kBK * D / 8 / kThreads;           // 16-byte K chunks per thread
-  static constexpr int VBL = (kBK / 4) * (D / 8);              // 4-key x 8-column V blocks per tile
-  static constexpr int VPT = (VBL + kThreads - 1) / kThreads;  // V blocks per thread
+  static constexpr int KCH = kBK * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
+  static constexpr int kRowStep = kThreads / (D / 8);  // tokens between a thread's chunks
   uint4 kr[KCH];
-  uint4 vr[VPT][4];
+  uint4 vr[KCH];
 };
 
-// Per-thread byte offsets of the staging loads. Thread tid loads K chunks
-// id = tid + j*kThreads (key id/(D/8), 16-byte column id%(D/8)); since
-// kThreads is a multiple of D/8 these are k0 + j*kKeyStep rows apart. Its V
-// block (4 keys from 4*(tid % 16), 8 columns from 8*(tid / 16)) starts at v0.
 template <int D>
-struct TileOffsets {
-  static constexpr int kKeyStep = kThreads / (D / 8);
-  uint32_t k0, v0;
-  __device__ TileOffsets(int tid, uint32_t row_bytes) {
-    k0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
-    v0 = (uint32_t)(4 * (tid % (kBK / 4))) * row_bytes + (uint32_t)(tid / (kBK / 4)) * 16u;
+__device__ __forceinline__ void load_tile(TileRegs<D>& r, uint32_t off0, rsrc_t kr, rsrc_t vr,
+                                          uint32_t row_bytes) {
+#pragma unroll
+  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
+    const uint32_t off = off0 + (uint32_t)(j * TileRegs<D>::kRowStep) * row_bytes;
+    r.kr[j] = buf_load16(kr, off);
+    r.vr[j] = buf_load16(vr, off);
   }
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, const TileOffsets<D>& off, rsrc_t kr, rsrc_t vr,
-                                          uint32_t row_bytes, int tid) {
-  static_assert(TileRegs<D>::VPT == 1, "one V block per thread");
-#pragma unroll
-  for (int j = 0; j < TileRegs<D>::KCH; ++j)
-    r.kr[j] = buf_load16(kr, off.k0 + (uint32_t)(j * TileOffsets<D>::kKeyStep) * row_bytes);
-  if (tid < TileRegs<D>::VBL)
-#pragma unroll
-    for (int x = 0; x < 4; ++x) r.vr[0][x] = buf_load16(vr, off.v0 + x * row_bytes);
 }
 
 template <int D>
 __device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16* vs, int tid) {
-  using S = FwdSmem<D>;
+  using L = RowTile<D>;
 #pragma unroll
   for (int j = 0; j < TileRegs<D>::KCH; ++j) {
-    const int id = tid + j * kThreads;
-    *reinterpret_cast<uint4*>(ks + (id / (D / 8)) * S::KS + (id % (D / 8)) * 8) = r.kr[j];
-  }
-#pragma unroll
-  for (int j = 0; j < TileRegs<D>::VPT; ++j) {
-    const int id = tid + j * kThreads;
-    if (id < TileRegs<D>::VBL) {
-      const int kg = id % (kBK / 4), cg = id / (kBK / 4);
-      // 4 keys x 8 columns -> 8 rows of V^T holding 4 consecutive keys each
-      const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&r.vr[j][0]);
-      const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&r.vr[j][1]);
-      const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&r.vr[j][2]);
-      const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&r.vr[j][3]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const int wi = c >> 1;
-        const uint32_t lo = (c & 1) ? pack_hi16(w0[wi], w1[wi]) : pack_lo16(w0[wi], w1[wi]);
-        const uint32_t hi = (c & 1) ? pack_hi16(w2[wi], w3[wi]) : pack_lo16(w2[wi], w3[wi]);
-        *reinterpret_cast<uint2*>(vs + (cg * 8 + c) * S::VS + kg * 4) = make_uint2(lo, hi);
-      }
-    }
+    const int at = L::off(tid / (D / 8) + j * TileRegs<D>::kRowStep, (tid % (D / 8)) * 8);
+    *reinterpret_cast<uint4*>(ks + at) = r.kr[j];
+    *reinterpret_cast<uint4*>(vs + at) = r.vr[j];
   }
 }
 
@@ -204,12 +172,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
-  const TileOffsets<D> off(tid, row_bytes);
+  const uint32_t off0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
   TileRegs<D> tr;
   auto rsrc_at = [&](const bf16* p, int kt0) {
     return make_rsrc(p + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
   };
-  load_tile<D>(tr, off, rsrc_at(kb, s), rsrc_at(vb, s), row_bytes, tid);
+  load_tile<D>(tr, off0, rsrc_at(kb, s), rsrc_at(vb, s), row_bytes);
   store_tile<D>(tr, smem, smem + S::K_ELEMS, tid);
   __syncthreads();
 
@@ -218,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     const bf16* ks = smem + (t & 1) * S::STAGE;
     const bf16* vs = ks + S::K_ELEMS;
     const bool more = t + 1 < ntiles;
-    if (more) load_tile<D>(tr, off, rsrc_at(kb, kt0 + kBK), rsrc_at(vb, kt0 + kBK), row_bytes, tid);
+    if (more) load_tile<D>(tr, off0, rsrc_at(kb, kt0 + kBK), rsrc_at(vb, kt0 + kBK), row_bytes);
 
     const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
     if (wave_active) {
@@ -230,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const uint4 av = *reinterpret_cast<const uint4*>(ks + (blk * 32 + l32) * S::KS + 16 * kk + 8 * half);
+          const uint4 av = *reinterpret_cast<const uint4*>(ks + S::L::off(blk * 32 + l32, 16 * kk + 8 * half));
           sacc[blk] = mfma32(as_bf16x8(av), as_bf16x8(qreg[kk]), sacc[blk]);
         }
       }
@@ -284,19 +252,14 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
                                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         }
 
-      // O^T += V^T P^T. MFMA k index 8*half + j of step (blk, mm) is key
-      // blk*32 + 16*mm + 4*half + j (j < 4) or blk*32 + 16*mm + 8 + 4*half + (j - 4).
+      // O^T += V^T P^T: the A operand is V^T read from the row-major V tile
+      // with transposing reads; step (blk, mm) covers keys blk*32 + 16*mm ..
+      // +15 in the accumulator's row order, which is how P^T sits in pb.
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const bf16* vrow = vs + (cb * 32 + l32) * S::VS + 4 * half;
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int koff = (st >> 1) * 32 + (st & 1) * 16;
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + koff);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + koff + 8);
-          oacc[cb] = mfma32(as_bf16x8(make_bf16x8_bits(lo, hi)), as_bf16x8(pb[st]), oacc[cb]);
-        }
-      }
+        for (int st = 0; st < 4; ++st)
+          oacc[cb] = mfma32(a_from_rows<D>(vs, 16 * st, 32 * cb, lane), as_bf16x8(pb[st]), oacc[cb]);
     }
 
     if (more) store_tile<D>(tr, smem + ((t + 1) & 1) * S::STAGE, smem + ((t + 1) & 1) * S::STAGE + S::K_ELEMS, tid);

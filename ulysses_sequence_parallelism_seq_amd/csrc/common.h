@@ -68,6 +68,62 @@ __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __builtin_bit_cast(float, bits16 << 16);
 }
 
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Transposing LDS read (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunks addressed by lanes
+// 4m + i/4 of its group, for m = 0..3 (layout checked on gfx950).
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16* p) {
+  const lds_v4i16* a = (const lds_v4i16*)(const __attribute__((address_space(3))) void*)(p);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16*>(a)));
+}
+
+// Layout of a [token][d] bf16 tile in LDS. For d = 128 the rows are 256 bytes,
+// unpadded, and the 16-byte chunk c of row r sits at chunk c ^ swz(r). swz
+// makes three access patterns free of bank conflicts (with 32 or 64 banks):
+// 16-byte reads of one chunk from 16 consecutive rows (MFMA operands), the
+// transposing reads of a_from_rows (4 rows x 4 half-chunks per 16 lanes),
+// and 16-byte stores of whole rows (staging). For d = 64 the rows are padded
+// by 16 bytes instead.
+__host__ __device__ constexpr int swz(int r) { return ((10 * (r & 3)) & 15) ^ ((r >> 2) & 3); }
+
+// swz permutes the 16 chunks of a 256-byte row (a chunk never leaves its row).
+constexpr bool swz_stays_in_row() {
+  for (int r = 0; r < 16; ++r)
+    for (int c = 0; c < 16; ++c)
+      if ((c ^ swz(r)) < 0 || (c ^ swz(r)) > 15) return false;
+  return true;
+}
+static_assert(swz_stays_in_row(), "swizzled chunk index must stay within the row");
+
+template <int D>
+struct RowTile {
+  static constexpr bool kSwizzle = (D == 128);
+  static constexpr int RS = kSwizzle ? D : D + 8;  // row stride (bf16 elements)
+  // element offset of (row, col); col is a multiple of 4
+  __device__ static __forceinline__ int off(int row, int col) {
+    if (kSwizzle) return row * RS + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
+    return row * RS + col;
+  }
+};
+
+// MFMA A operand (rows = 32 columns c0 .. c0+31 of a [token][d] LDS tile in
+// the RowTile layout; k = 16 tokens from t0) read with two transposing
+// reads. Lane l (h = l / 32) receives column c0 + l % 32 of tokens
+// t0 + 4h + (0..3) and t0 + 8 + 4h + (0..3): MFMA k index 8h + j is token
+// t0 + 4h + j (j < 4) or t0 + 8 + 4h + (j - 4), the same token order as an
+// accumulator's rows.
+template <int D>
+__device__ __forceinline__ bf16x8 a_from_rows(const bf16* tile, int t0, int c0, int lane) {
+  const int p = lane & 15;
+  const int row = t0 + 4 * (lane >> 5) + (p >> 2);
+  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (p & 3);
+  const uint2 lo = lds_read_tr16(tile + RowTile<D>::off(row, col));
+  const uint2 hi = lds_read_tr16(tile + RowTile<D>::off(row + 8, col));
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // Value held by lane (l ^ 32) of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -1,0 +1,98 @@
+"""HBM traffic of the attention backward from rocprofv3 counter runs.
+
+Two counter runs of bench.py (one with FETCH_SIZE, one with WRITE_SIZE, in
+KiB per dispatch) give the bytes each kernel moved between L2 and memory. The
+counters are calibrated with the permute kernel of the same run, a plain copy
+whose bytes are known (it reads and writes every element once), and the
+figures are stored with a hash of the kernel sources so a later change of the
+kernels invalidates them.
+
+  python -m ulysses_sequence_parallelism_seq_amd.traffic FETCH_DIR WRITE_DIR OUT.txt "COMMANDS"
+
+reads the two counter_collection.csv files and writes OUT.txt; bench.py
+calls read_traffic(OUT.txt) to fill its roofline "traffic" field.
+"""
+
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import os
+import sys
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCES = ["csrc/attn_bwd.hip", "csrc/common.h", "csrc/permute.hip"]
+BWD_KERNELS = ("attn_dkdv_bf16_kernel<128>", "attn_dq_bf16_kernel<128>", "delta_bf16_kernel<128>")
+COPY_KERNEL = "permute_runs<true>"
+
+
+def sources_sha256() -> str:
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(_HERE, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _short(name: str) -> str:
+    return name.replace("void (anonymous namespace)::", "").replace("void ", "").split("(")[0]
+
+
+def _per_dispatch(csv_dir: str, counter: str) -> dict:
+    sums, counts = {}, {}
+    for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for row in csv.DictReader(f):
+                if row["Counter_Name"] != counter:
+                    continue
+                k = _short(row["Kernel_Name"])
+                sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
+                counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def write_traffic(fetch_dir: str, write_dir: str, out: str, commands: str, copy_bytes: int) -> None:
+    fetch = _per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _per_dispatch(write_dir, "WRITE_SIZE")
+    lines = [
+        "# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB), long workload",
+        f"# commands: {commands}",
+        f"source_sha256 {sources_sha256()}",
+        f"copy {COPY_KERNEL} bytes={copy_bytes} fetch_kib={fetch[COPY_KERNEL]:.1f} write_kib={write[COPY_KERNEL]:.1f}",
+    ]
+    for k in BWD_KERNELS:
+        lines.append(f"kernel {k} fetch_kib={fetch[k]:.1f} write_kib={write[k]:.1f}")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def read_traffic(path: str):
+    """Calibrated bytes of one attention-backward call, or None if stale or missing."""
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#"):
+                continue
+            if parts[0] == "source_sha256":
+                rec["sha"] = parts[1]
+            elif parts[0] in ("copy", "kernel"):
+                rec[(parts[0], parts[1])] = dict(p.split("=") for p in parts[2:])
+    if rec.get("sha") != sources_sha256():
+        return None
+    copy = next(v for (kind, _), v in rec.items() if kind == "copy")
+    copy_kib = float(copy["bytes"]) / 1024.0  # the copy reads this many KiB and writes as many
+    f_scale = copy_kib / float(copy["fetch_kib"])
+    w_scale = copy_kib / float(copy["write_kib"])
+    total = 0.0
+    for (kind, _), v in rec.items():
+        if kind == "kernel":
+            total += float(v["fetch_kib"]) * f_scale + float(v["write_kib"]) * w_scale
+    return {"bytes": total * 1024.0, "fetch_scale": f_scale, "write_scale": w_scale}
+
+
+if __name__ == "__main__":
+    write_traffic(sys.argv[1], sys.argv[2], sys.argv[3], sys.argv[4], int(sys.argv[5]))
