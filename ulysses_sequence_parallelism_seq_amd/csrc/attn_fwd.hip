@@ -9,8 +9,8 @@
 // mask allowing key j for query i iff both sit in the same document and
 // (not causal or j <= i).
 //
-// Kernel design (one workgroup = 4 waves = a tile of 128 queries of one
-// document of one (row, head)):
+// Kernel design (one workgroup = 8 waves = a tile of 256 queries of one
+// document of one (row, head); the waves share each staged K/V tile):
 //   * Each wave owns 32 queries. It computes S^T = K Q^T with the 32x32x16
 //     bf16 MFMA: K (A operand) comes from LDS, Q^T (B operand) stays in
 //     registers for the whole kernel. In the S^T accumulator layout a lane
@@ -48,9 +48,9 @@ namespace {
 
 using namespace uly;
 
-constexpr int kBQ = 128;  // queries per workgroup
+constexpr int kBQ = 256;  // queries per workgroup (32 per wave)
 constexpr int kBK = 64;   // keys per K/V tile
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;  // 8 waves sharing each K/V tile
 
 template <int D>
 struct FwdSmem {
@@ -119,7 +119,7 @@ __device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16*
 constexpr float kRescaleSlack = 8.0f;
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   using S = FwdSmem<D>;
   constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
   constexpr int CB = D / 32;  // 32-wide column blocks of O^T
@@ -190,10 +190,11 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
     const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
     if (wave_active) {
-      // S^T for two 32-key blocks
-      f32x16 sacc[2];
+      // S^T for the tile's 32-key blocks
+      constexpr int NB = kBK / 32;
+      f32x16 sacc[NB];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
+      for (int blk = 0; blk < NB; ++blk) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
 #pragma unroll
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       float mloc = -INFINITY;
       if (need_mask) {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             float x = sacc[blk][i];
@@ -218,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           }
       } else {
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
+        for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             mloc = fmaxf(mloc, sacc[blk][i]);
@@ -237,9 +238,9 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
 
       // P^T = exp2(x - m), packed to bf16 as the B operand of four 16-key MFMA steps
-      uint4 pb[4];
+      uint4 pb[2 * NB];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
           float p[8];
@@ -258,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+        for (int st = 0; st < 2 * NB; ++st)
           oacc[cb] = mfma32(a_from_rows<D>(vs, 16 * st, 32 * cb, lane), as_bf16x8(pb[st]), oacc[cb]);
     }
 

@@ -79,13 +79,13 @@ __device__ __forceinline__ uint2 lds_read_tr16(const bf16* p) {
   return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(const_cast<lds_v4i16*>(a)));
 }
 
-// Layout of a [token][d] bf16 tile in LDS. For d = 128 the rows are 256 bytes,
-// unpadded, and the 16-byte chunk c of row r sits at chunk c ^ swz(r). swz
-// makes three access patterns free of bank conflicts (with 32 or 64 banks):
-// 16-byte reads of one chunk from 16 consecutive rows (MFMA operands), the
-// transposing reads of a_from_rows (4 rows x 4 half-chunks per 16 lanes),
-// and 16-byte stores of whole rows (staging). For d = 64 the rows are padded
-// by 16 bytes instead.
+// Layout of a [token][d] bf16 tile in LDS: unpadded rows of 2d bytes whose
+// 16-byte chunk c sits at chunk c ^ swz(r) (for d = 64 the low 3 bits of
+// swz). swz makes three access patterns free of bank conflicts (with 32 or
+// 64 banks): 16-byte reads of one chunk from 16 consecutive rows (MFMA
+// operands), the transposing reads of a_from_rows (4 rows x 4 half-chunks
+// per 16 lanes) and 16-byte stores of whole rows (staging). Unpadded rows
+// also let a wave's direct-to-LDS load fill whole rows.
 __host__ __device__ constexpr int swz(int r) { return ((10 * (r & 3)) & 15) ^ ((r >> 2) & 3); }
 
 // swz permutes the 16 chunks of a 256-byte row (a chunk never leaves its row).
@@ -99,12 +99,12 @@ static_assert(swz_stays_in_row(), "swizzled chunk index must stay within the row
 
 template <int D>
 struct RowTile {
-  static constexpr bool kSwizzle = (D == 128);
-  static constexpr int RS = kSwizzle ? D : D + 8;  // row stride (bf16 elements)
+  static constexpr int RS = D;           // row stride (bf16 elements)
+  static constexpr int CHUNKS = D / 8;   // 16-byte chunks per row
+  __device__ static __forceinline__ int chunk_key(int row) { return swz(row) & (CHUNKS - 1); }
   // element offset of (row, col); col is a multiple of 4
   __device__ static __forceinline__ int off(int row, int col) {
-    if (kSwizzle) return row * RS + ((((col >> 3) ^ swz(row)) << 3) | (col & 7));
-    return row * RS + col;
+    return row * RS + ((((col >> 3) ^ chunk_key(row)) << 3) | (col & 7));
   }
 };
 
