@@ -101,9 +101,9 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int Hl, int d, int causal, int dtype, void* stream);
 
 /*
- * Bytes of device workspace ulysses_attn_bwd needs: one float per (rank,
- * batch row, head, token), i.e. O(N), never O(N^2). Returns 0 for invalid
- * arguments.
+ * Bytes of device workspace ulysses_attn_bwd needs: two floats per (rank,
+ * batch row, head, token) (the row sums D = rowsum(dO * O) and lse in log2
+ * units), i.e. O(N), never O(N^2). Returns 0 for invalid arguments.
  */
 size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype);
 

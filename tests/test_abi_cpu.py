@@ -75,7 +75,7 @@ def test_attention_argument_errors():
 
     bwd = lib.ulysses_attn_bwd
     need = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 64, 1)
-    assert need == 1 * 1 * 2 * 8 * 4
+    assert need == 2 * 1 * 1 * 2 * 8 * 4  # D and lse in log2 units, one float each per (unit, token)
     assert lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 48, 1) == 0
     ptrs = [FAKE] * 9
     assert bwd(*ptrs, FAKE, need - 1, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
@@ -88,7 +88,7 @@ def test_workspace_is_linear_in_n():
     lib = uly.library()
     w1 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 131072, 4, 128, 1)
     w2 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 262144, 4, 128, 1)
-    assert w2 == 2 * w1 == 2 * 131072 * 4 * 4
+    assert w2 == 2 * w1 == 2 * 2 * 131072 * 4 * 4
 
 
 def test_binding_rejects_host_tensors():

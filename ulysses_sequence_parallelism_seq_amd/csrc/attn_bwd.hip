@@ -47,7 +47,8 @@ struct BwdArgs {
   const bf16* o;
   const bf16* dout;
   const float* lse;
-  float* delta;
+  float* delta;  // workspace: D, then lse in log2 units (units * N floats each)
+  float* lse2;
   bf16* dq;
   bf16* dk;
   bf16* dv;
@@ -73,10 +74,13 @@ __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int
 
 // ------------------------------------------------------------------ D pre-pass
 // D[unit][t] = sum_c dO[t][c] * O[t][c]; D/8 lanes per row, 16 bytes per lane.
+// Also lse2[unit][t] = lse[unit][t] * log2(e), the form the dK/dV kernel stages.
 template <int D>
 __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __restrict__ o,
                                                               const bf16* __restrict__ dout,
-                                                              float* __restrict__ delta, int N, int Hl,
+                                                              const float* __restrict__ lse,
+                                                              float* __restrict__ delta,
+                                                              float* __restrict__ lse2, int N, int Hl,
                                                               long long rows) {
   constexpr int LPR = D / 8;  // lanes per row
   constexpr int RPB = kThreads / LPR;
@@ -102,7 +106,10 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
   }
 #pragma unroll
   for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && sub == 0) delta[row] = acc;
+  if (row < rows && sub == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ----------------------------------------------------------- shared tile staging
@@ -151,11 +158,8 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
   constexpr int STAGE = 2 * TILE;    // K then V
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
 
-  const int per_level = a.ndoc * a.units;
-  const int lvl = blockIdx.x / per_level;
-  const int rem = blockIdx.x - lvl * per_level;
-  const int doc = rem / a.units;
-  const int unit = rem - doc * a.units;
+  const TileId tid_ = decode_tile(blockIdx.x, a.nslots, a.ndoc, a.units);
+  const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
   int s, e;
   doc_range(a, doc, s, e);
   const int q0 = s + (a.nslots - 1 - lvl) * kDqBQ;
@@ -274,32 +278,88 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------- dkdv kernel
-// 8 waves, 128 keys per workgroup. Waves w and w + 4 share the 32 keys
-// kb0 + 32*(w % 4): each computes S, dP, P and dS for one of the tile's two
-// 32-query blocks (block w / 4), hands its packed P and dS to the other wave
-// through LDS, and accumulates dK and dV for one half of the head dimension
-// (columns [w/4 * D/2, w/4 * D/2 + D/2)) over both blocks. No MFMA is done
-// twice, and with half the accumulators per wave two waves fit on a SIMD.
-constexpr int kKvBK = 128;      // keys per workgroup
-constexpr int kKvBQ = 64;       // queries per tile (two 32-query blocks)
-constexpr int kKvThreads = 512; // 8 waves
+// A workgroup owns 128 keys and walks 64-query tiles from the document end
+// down to its first key (causal). Its 8 waves come in pairs that share a SIMD
+// (waves p and p + 4) and 32 keys:
+//   * producer p: K^T and V^T of the 32 keys stay in registers as B operands;
+//     per tile it computes S = Q K^T and dP = dO V^T for both 32-query blocks
+//     (lane = key), then P = exp2(S * log2(e) / sqrt(d) - lse2) and
+//     dS = P (dP - D), packed to bf16 in the order the MFMA k index takes them;
+//   * consumer p + 4: one tile behind, dV^T += dO^T P and dK^T += Q^T dS for
+//     all D columns of the 32 keys, with the A operands read transposed from
+//     the row-major Q and dO tiles and P, dS taken from the producer through LDS.
+// The producer's exponentials run while the consumer keeps the SIMD's matrix
+// core busy. Query tiles (Q, dO, lse2, D) arrive by direct-to-LDS loads one
+// tile ahead, in three stages: the producer reads tile i while the consumer
+// reads tile i - 1 and tile i + 1 lands. Two barriers per tile: after the
+// first the producer overwrites the P/dS buffer the consumer has read, after
+// the second the new P/dS and tile i + 1 are visible.
+constexpr int kKvBK = 128;       // keys per workgroup
+constexpr int kKvBQ = 64;        // queries per tile (two 32-query blocks)
+constexpr int kKvThreads = 512;  // 4 producer and 4 consumer waves
+
+template <int D>
+struct KvStage {
+  bf16 q[kKvBQ * D];     // RowTile layout
+  bf16 dout[kKvBQ * D];  // RowTile layout
+  float lse2[kKvBQ];
+  float dlt[kKvBQ];
+};
+
+// Direct-to-LDS loads of one query tile: the 2 * kKvBQ rows of Q and dO are
+// dealt to the 8 waves in 1 KB windows (waves 0-3 take Q, 4-7 dO); lane i
+// lands on physical chunk i % (D/8) of its row and fetches the logical chunk
+// the swizzle keeps there. Waves 0 and 1 also fetch lse2 and D, 4 bytes a
+// lane. Buffer ranges end at the document end (zeros past it).
+template <int D>
+struct KvDma {
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int ROWS_PER_OP = 64 / CHUNKS;
+  static constexpr int OPS_PER_TENSOR = kKvBQ / ROWS_PER_OP;
+  static constexpr int OPS = 2 * OPS_PER_TENSOR / (kKvThreads / 64);
+  static_assert(OPS >= 1 && OPS * (kKvThreads / 64) == 2 * OPS_PER_TENSOR, "whole windows per wave");
+  uint32_t voff[OPS];
+  int lds_off[OPS];  // bf16 elements from the start of the tensor's tile
+  bool is_dout;
+
+  __device__ __forceinline__ void init(int w, int lane, uint32_t row_bytes) {
+    is_dout = w >= (kKvThreads / 64) / 2;
+#pragma unroll
+    for (int j = 0; j < OPS; ++j) {
+      const int op = (w * OPS + j) % OPS_PER_TENSOR;
+      const int row0 = op * ROWS_PER_OP;
+      const int r = row0 + lane / CHUNKS;
+      const int c = (lane % CHUNKS) ^ RowTile<D>::chunk_key(r);
+      voff[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
+      lds_off[j] = row0 * D;
+    }
+  }
+  __device__ __forceinline__ void issue(rsrc_t rq, rsrc_t rd, rsrc_t rl, rsrc_t rdl, KvStage<D>& st, int w,
+                                        int lane) const {
+    const bf16* dst = is_dout ? st.dout : st.q;
+    const rsrc_t src = is_dout ? rd : rq;
+#pragma unroll
+    for (int j = 0; j < OPS; ++j) buf_load16_lds(src, dst + lds_off[j], voff[j]);
+    if (w == 0) buf_load4_lds(rl, st.lse2, (uint32_t)lane * 4u);
+    if (w == 1) buf_load4_lds(rdl, st.dlt, (uint32_t)lane * 4u);
+  }
+};
 
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) {
-  using T = PairTile<D, kKvBQ, kKvThreads>;
+  using L = RowTile<D>;
   constexpr int KK = D / 16;
-  constexpr int CBH = D / 64;                 // 32-column blocks per wave (half of D / 32)
-  constexpr int TILE = kKvBQ * T::RS;         // bf16 elements of one staged tensor
-  constexpr int STAGE_BYTES = 2 * TILE * 2 + 2 * kKvBQ * 4;  // Q, dO, then lse (log2 units) and D
-  constexpr int XCH_BYTES = 8 * 4 * 64 * 16;  // per wave: P and dS as 4 x 16 bytes per lane
-  __shared__ __attribute__((aligned(16))) uint8_t smem_raw[2 * STAGE_BYTES + XCH_BYTES];
-  uint4* xch = reinterpret_cast<uint4*>(smem_raw + 2 * STAGE_BYTES);
+  constexpr int CB = D / 32;
+  // Three query-tile stages, separate arrays so that the compiler can tell a
+  // stage being loaded from the stages being read.
+  __shared__ __attribute__((aligned(16))) KvStage<D> st0;
+  __shared__ __attribute__((aligned(16))) KvStage<D> st1;
+  __shared__ __attribute__((aligned(16))) KvStage<D> st2;
+  // P and dS of the last tile: per producer, per query block, 4 MFMA operands of 64 lanes
+  __shared__ __attribute__((aligned(16))) uint4 xbuf[4 * 2 * 4 * 64];
 
-  const int per_level = a.ndoc * a.units;
-  const int lvl = blockIdx.x / per_level;
-  const int rem = blockIdx.x - lvl * per_level;
-  const int doc = rem / a.units;
-  const int unit = rem - doc * a.units;
+  const TileId tid_ = decode_tile(blockIdx.x, a.nslots, a.ndoc, a.units);
+  const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
   int s, e;
   doc_range(a, doc, s, e);
   const int kb0 = s + lvl * kKvBK;  // causal: low key blocks have the most queries, so they go first
@@ -311,157 +371,194 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const int kgrp = w & 3, role = w >> 2;  // key group; query block and column half of this wave
-  const int kj = kb0 + 32 * kgrp + l32;
-
-  // K^T and V^T of the wave's 32 keys as resident B operands (zero past the document end)
-  uint4 kreg[KK], vreg[KK];
-  {
-    const long long span = (long long)(e - kb0) * row_bytes;
-    const rsrc_t kr = make_rsrc(a.k + base + (size_t)kb0 * rs, span);
-    const rsrc_t vr = make_rsrc(a.v + base + (size_t)kb0 * rs, span);
-    const uint32_t off = (uint32_t)(32 * kgrp + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      kreg[kk] = buf_load16(kr, off + 32u * kk);
-      vreg[kk] = buf_load16(vr, off + 32u * kk);
-    }
-  }
+  const bool producer = w < 4;
+  const int pair = w & 3;
+  const int kp0 = kb0 + 32 * pair;  // the pair's first key
+  const int kj = kp0 + l32;         // this lane's key
 
   const int qstart = a.causal ? kb0 : s;
   const int ntiles = (e - qstart + kKvBQ - 1) / kKvBQ;
-  const float* lse_u = a.lse + (size_t)unit * a.N;
-  const float* dl_u = a.delta + (size_t)unit * a.N;
-
-  f32x16 dkacc[CBH], dvacc[CBH];
-#pragma unroll
-  for (int c = 0; c < CBH; ++c)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dkacc[c][i] = dvacc[c][i] = 0.f;
-
-  // staging: Q and dO chunks; threads [0, 64) also carry the tile's lse (log2
-  // units), threads [64, 128) its D
-  const uint32_t off0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
-  T tile;
-  float sv = 0.f;
-  auto load = [&](int qt0) {
-    const long long span = (long long)(e - qt0) * row_bytes;
-    tile.load(make_rsrc(a.q + base + (size_t)qt0 * rs, span), make_rsrc(a.dout + base + (size_t)qt0 * rs, span),
-              off0, row_bytes);
-    if (tid < 2 * kKvBQ) {
-      const int qq = qt0 + (tid % kKvBQ);
-      if (tid < kKvBQ) sv = qq < e ? lse_u[qq] * kLog2e : 0.f;
-      else sv = qq < e ? dl_u[qq] : 0.f;
-    }
-  };
-  auto store = [&](uint8_t* stage) {
-    bf16* sm = reinterpret_cast<bf16*>(stage);
-    tile.store(sm, sm + TILE, tid);
-    if (tid < 2 * kKvBQ) reinterpret_cast<float*>(stage + 2 * TILE * 2)[tid] = sv;
-  };
-
-  // Query tiles are walked from the document end down to the first one this
-  // block needs: every workgroup of a head then reads the same Q/dO tile at
-  // about the same time, so the XCD's L2 serves them all.
+  // Query tiles are walked from the document end down: every workgroup of a
+  // head then reads the same tile at about the same time, from the XCD's L2.
   const int qlast = qstart + (ntiles - 1) * kKvBQ;
-  load(qlast);
-  store(smem_raw);
-  __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
-    const int qt0 = qlast - t * kKvBQ;
-    const uint8_t* stage = smem_raw + (t & 1) * STAGE_BYTES;
-    const bf16* qs = reinterpret_cast<const bf16*>(stage);
-    const bf16* dos = qs + TILE;
-    const float* sf = reinterpret_cast<const float*>(stage + 2 * TILE * 2);
-    const bool more = t + 1 < ntiles;
-    if (more) load(qt0 - kKvBQ);
+  KvDma<D> dma;
+  dma.init(w, lane, row_bytes);
+  const float* lse2_u = a.lse2 + (size_t)unit * a.N;
+  const float* dl_u = a.delta + (size_t)unit * a.N;
+  auto load_tile = [&](int i, KvStage<D>& st) {
+    const int qt0 = qlast - i * kKvBQ;
+    const long long span = (long long)(e - qt0) * row_bytes;
+    dma.issue(make_rsrc(a.q + base + (size_t)qt0 * rs, span), make_rsrc(a.dout + base + (size_t)qt0 * rs, span),
+              make_rsrc(lse2_u + qt0, (long long)(e - qt0) * 4), make_rsrc(dl_u + qt0, (long long)(e - qt0) * 4),
+              st, w, lane);
+  };
 
-    // ---- this wave's query block: S = Q K^T, dP = dO V^T (lane = key kj,
-    // element i is query qb0 + 8*(i/4) + 4*half + (i%4)), then P and dS
-    const int qb0 = qt0 + 32 * role;
-    f32x16 sacc, pacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int off = RowTile<D>::off(32 * role + l32, 16 * kk + 8 * half);
-      const uint4 qa = *reinterpret_cast<const uint4*>(qs + off);
-      const uint4 da = *reinterpret_cast<const uint4*>(dos + off);
-      sacc = mfma32(as_bf16x8(qa), as_bf16x8(kreg[kk]), sacc);
-      pacc = mfma32(as_bf16x8(da), as_bf16x8(vreg[kk]), pacc);
+  // The tile loop, with the three stages named per iteration (i mod 3):
+  // work(i, cur, prev) runs between the loads of tile i + 1 going out and the
+  // first barrier, publish(i) between the two barriers. Producers and
+  // consumers run it with their own bodies, so that each role's registers are
+  // its own; both pass the same barriers.
+  auto tile_loop = [&](auto work, auto publish) {
+    auto iteration = [&](int i, const KvStage<D>& cur, const KvStage<D>& prev, KvStage<D>& next) {
+      if (i + 1 < ntiles) load_tile(i + 1, next);
+      work(i, cur, prev);
+      barrier_lds_only();  // the consumer has read the P/dS buffer
+      publish(i);
+      wait_vmem();
+      __syncthreads();  // new P/dS and tile i + 1 visible
+    };
+    load_tile(0, st0);
+    wait_vmem();
+    __syncthreads();
+    for (int i = 0; i <= ntiles; i += 3) {
+      iteration(i, st0, st2, st1);
+      if (i + 1 <= ntiles) iteration(i + 1, st1, st0, st2);
+      if (i + 2 <= ntiles) iteration(i + 2, st2, st1, st0);
     }
-    // tiles that cross the diagonal or a document end are masked element by element
-    const bool need_mask = (a.causal && qt0 < kb0 + kKvBK - 1) || qt0 + kKvBQ > e || kb0 + kKvBK > e;
-    float p[16], ds[16];
+  };
+
+  if (producer) {
+    // K^T and V^T of the pair's 32 keys (zero past the document end)
+    uint4 kreg[KK], vreg[KK];
+    {
+      const long long span = (long long)(e - kp0) * row_bytes;
+      const rsrc_t kr = make_rsrc(a.k + base + (size_t)kp0 * rs, span);
+      const rsrc_t vr = make_rsrc(a.v + base + (size_t)kp0 * rs, span);
+      const uint32_t off = (uint32_t)l32 * row_bytes + (uint32_t)(8 * half) * 2u;
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const float4 l4 = *reinterpret_cast<const float4*>(sf + 32 * role + 8 * gq + 4 * half);
-      const float4 d4 = *reinterpret_cast<const float4*>(sf + kKvBQ + 32 * role + 8 * gq + 4 * half);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int i = 4 * gq + x;
-        p[i] = fast_exp2(fmaf(sacc[i], a.sl2, -lv[x]));
-        ds[i] = pacc[i] - dv[x];
+      for (int kk = 0; kk < KK; ++kk) {
+        kreg[kk] = buf_load16(kr, off + 32u * kk);
+        vreg[kk] = buf_load16(vr, off + 32u * kk);
       }
     }
-    if (need_mask) {
+    // P and dS of both query blocks as MFMA B operands: pk[4 qb + mm] = P,
+    // pk[4 qb + 2 + mm] = dS, accumulator elements 8 mm .. 8 mm + 7
+    uint4 pk[8];
+    auto produce = [&](int i, const KvStage<D>& st, const KvStage<D>&) {
+      if (i >= ntiles) return;
+      const int qt0 = qlast - i * kKvBQ;
+      // tiles that cross the diagonal or a document end are masked element by element
+      const bool need_mask = (a.causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int qq = qb0 + 8 * (i >> 2) + 4 * half + (i & 3);
-        if (qq >= e || kj >= e || (a.causal && kj > qq)) p[i] = 0.f;
-      }
-    }
-    // P then dS, each as two MFMA steps (accumulator elements 8*mm .. 8*mm+7),
-    // published for the partner wave (and read back by this one below)
+      for (int qb = 0; qb < 2; ++qb) {
+        f32x16 sacc, pacc;
 #pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const int b = 8 * mm;
-      xch[(w * 4 + mm) * 64 + lane] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
-                                                 pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
-      xch[(w * 4 + 2 + mm) * 64 + lane] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
-                                                     pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
-                                                     pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
-                                                     pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
-    }
-    __syncthreads();  // both blocks' P and dS are visible
-
-    // ---- dV^T += dO^T P and dK^T += Q^T dS over both query blocks, for this
-    // wave's half of the columns; A operands by transposing reads of dO and Q
+        for (int x = 0; x < 16; ++x) sacc[x] = pacc[x] = 0.f;
+        // Q and dO fragments read two k-steps ahead of their MFMAs
+        auto rd = [&](int kk, uint4* f) {
+          const int off = L::off(32 * qb + l32, 16 * kk + 8 * half);
+          f[0] = *reinterpret_cast<const uint4*>(st.q + off);
+          f[1] = *reinterpret_cast<const uint4*>(st.dout + off);
+        };
+        uint4 fr[3][2];
+        rd(0, fr[0]);
+        rd(1, fr[1]);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int owner = kgrp + 4 * qb;  // the wave that computed block qb for these keys
-      uint4 opnd[4];
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 2 < KK) rd(kk + 2, fr[(kk + 2) % 3]);
+          sacc = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc);
+          pacc = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        float p[16], ds[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) opnd[j] = xch[(owner * 4 + j) * 64 + lane];
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
+          const float4 d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-      for (int c = 0; c < CBH; ++c) {
-        const int c0 = 32 * (role * CBH + c);
+          for (int x = 0; x < 4; ++x) {
+            const int i2 = 4 * gq + x;
+            p[i2] = fast_exp2(fmaf(sacc[i2], a.sl2, -lv[x]));
+            ds[i2] = pacc[i2] - dv[x];
+          }
+        }
+        if (need_mask) {
+#pragma unroll
+          for (int x = 0; x < 16; ++x) {
+            const int qq = qt0 + 32 * qb + 8 * (x >> 2) + 4 * half + (x & 3);
+            if (qq >= e || kj >= e || (a.causal && kj > qq)) p[x] = 0.f;
+          }
+        }
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          dvacc[c] = mfma32(a_from_rows<D>(dos, 32 * qb + 16 * mm, c0, lane), as_bf16x8(opnd[mm]), dvacc[c]);
-          dkacc[c] = mfma32(a_from_rows<D>(qs, 32 * qb + 16 * mm, c0, lane), as_bf16x8(opnd[2 + mm]), dkacc[c]);
+          const int b = 8 * mm;
+          pk[4 * qb + mm] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
+                                       pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
+          pk[4 * qb + 2 + mm] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
+                                           pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
+                                           pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
+                                           pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
         }
       }
-    }
-
-    if (more) store(smem_raw + ((t + 1) & 1) * STAGE_BYTES);
-    __syncthreads();
-  }
-
-  if (kj < e) {
-    bf16* ko = a.dk + base + (size_t)kj * rs;
-    bf16* vo = a.dv + base + (size_t)kj * rs;
+    };
+    auto publish = [&](int i) {
+      if (i >= ntiles) return;
 #pragma unroll
-    for (int c = 0; c < CBH; ++c)
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int col = 32 * (role * CBH + c) + 8 * gq + 4 * half;
-        *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[c], 4 * gq, a.scale);
-        *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[c], 4 * gq, 1.f);
+        for (int j = 0; j < 4; ++j) xbuf[((pair * 2 + qb) * 4 + j) * 64 + lane] = pk[4 * qb + j];
+    };
+    tile_loop(produce, publish);
+  } else {
+    // dK^T and dV^T of the pair's 32 keys, all D columns (lane = key)
+    f32x16 dkacc[CB], dvacc[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) dkacc[c][i] = dvacc[c][i] = 0.f;
+    // the previous tile: dV^T += dO^T P and dK^T += Q^T dS over both query
+    // blocks. Step (qb, c) needs four A fragments (dO^T and Q^T, two 16-query
+    // halves); the fragments of the next step are read while this step's
+    // MFMAs run.
+    auto consume = [&](int i, const KvStage<D>&, const KvStage<D>& st) {
+      if (i < 1) return;
+      constexpr int NSTEP = 2 * CB;
+      auto rd = [&](int step, bf16x8* f) {
+        const int qb = step / CB, c = step % CB;
+        f[0] = a_from_rows<D>(st.dout, 32 * qb, 32 * c, lane);
+        f[1] = a_from_rows<D>(st.dout, 32 * qb + 16, 32 * c, lane);
+        f[2] = a_from_rows<D>(st.q, 32 * qb, 32 * c, lane);
+        f[3] = a_from_rows<D>(st.q, 32 * qb + 16, 32 * c, lane);
+      };
+      bf16x8 fr[2][4];
+      uint4 opnd[2][4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) opnd[0][j] = xbuf[((pair * 2 + 0) * 4 + j) * 64 + lane];
+      rd(0, fr[0]);
+#pragma unroll
+      for (int step = 0; step < NSTEP; ++step) {
+        const int qb = step / CB, c = step % CB;
+        if (step + 1 < NSTEP) rd(step + 1, fr[(step + 1) & 1]);
+        if (step == CB - 1) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) opnd[1][j] = xbuf[((pair * 2 + 1) * 4 + j) * 64 + lane];
+        }
+        const bf16x8* f = fr[step & 1];
+        dvacc[c] = mfma32(f[0], as_bf16x8(opnd[qb][0]), dvacc[c]);
+        dkacc[c] = mfma32(f[2], as_bf16x8(opnd[qb][2]), dkacc[c]);
+        dvacc[c] = mfma32(f[1], as_bf16x8(opnd[qb][1]), dvacc[c]);
+        dkacc[c] = mfma32(f[3], as_bf16x8(opnd[qb][3]), dkacc[c]);
+        // the reads of step + 1 stay ahead of these MFMAs, later ones stay behind
+        __builtin_amdgcn_sched_barrier(0);
       }
+    };
+    tile_loop(consume, [](int) {});
+
+    if (kj < e) {
+      bf16* ko = a.dk + base + (size_t)kj * rs;
+      bf16* vo = a.dv + base + (size_t)kj * rs;
+#pragma unroll
+      for (int c = 0; c < CB; ++c)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int col = 32 * c + 8 * gq + 4 * half;
+          *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[c], 4 * gq, a.scale);
+          *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[c], 4 * gq, 1.f);
+        }
+    }
   }
 }
 
@@ -480,6 +577,7 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   a.dout = static_cast<const bf16*>(dout);
   a.lse = lse;
   a.delta = delta;
+  a.lse2 = delta + (size_t)g.G * g.Hl * g.N;
   a.dq = static_cast<bf16*>(dq);
   a.dk = static_cast<bf16*>(dk);
   a.dv = static_cast<bf16*>(dv);
@@ -505,16 +603,19 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   BwdArgs akv = a;
   akv.nslots = (maxlen + kKvBK - 1) / kKvBK;
   const long long kvblocks = (long long)akv.nslots * a.ndoc * a.units;
-  if (qblocks > 0x7fffffffLL || kvblocks > 0x7fffffffLL) return ULY_ESHAPE;
+  // the tile decode also forms nslots * ndoc * kUnitGroup in int
+  const long long span_q = (long long)aq.nslots * a.ndoc * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
+  const long long span_kv = (long long)akv.nslots * a.ndoc * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
+  if (span_q > 0x7fffffffLL || span_kv > 0x7fffffffLL) return ULY_ESHAPE;
 
   if (g.d == 64) {
     hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
-                       delta, g.N, g.Hl, rows);
+                       lse, delta, a.lse2, g.N, g.Hl, rows);
     hipLaunchKernelGGL(attn_dkdv_bf16_kernel<64>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL(attn_dq_bf16_kernel<64>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, aq);
   } else {
     hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
-                       delta, g.N, g.Hl, rows);
+                       lse, delta, a.lse2, g.N, g.Hl, rows);
     hipLaunchKernelGGL(attn_dkdv_bf16_kernel<128>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL(attn_dq_bf16_kernel<128>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, aq);
   }
@@ -526,8 +627,8 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
 extern "C" size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype) {
   if (sp <= 0 || B <= 0 || N <= 0 || Hl <= 0) return 0;
   if (!uly_host::dtype_ok(dtype) || !uly_host::head_dim_ok(d)) return 0;
-  // D = rowsum(dO * O): one float per (rank, batch row, head, token).
-  return (size_t)sp * B * Hl * N * sizeof(float);
+  // D = rowsum(dO * O) and lse in log2 units: two floats per (rank, batch row, head, token).
+  return 2 * (size_t)sp * B * Hl * N * sizeof(float);
 }
 
 extern "C" int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -126,11 +126,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 smem[2 * S::STAGE];
 
   // ---- which tile
-  const int per_level = a.ndoc * a.units;
-  const int lvl = blockIdx.x / per_level;
-  const int rem = blockIdx.x - lvl * per_level;
-  const int doc = rem / a.units;
-  const int unit = rem - doc * a.units;
+  const TileId tid_ = decode_tile(blockIdx.x, a.nq_slots, a.ndoc, a.units);
+  const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
   const int qslot = a.nq_slots - 1 - lvl;
   int s = 0, e = a.N;
   if (a.cu) {
@@ -305,7 +302,9 @@ int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, f
   a.causal = g.causal;
   a.sl2 = uly::kLog2e / sqrtf((float)g.d);
   const long long blocks = (long long)a.nq_slots * a.ndoc * a.units;
-  if (blocks > 0x7fffffffLL) return ULY_ESHAPE;
+  // the tile decode also forms nq_slots * ndoc * kUnitGroup in int
+  const long long span = (long long)a.nq_slots * a.ndoc * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
+  if (span > 0x7fffffffLL) return ULY_ESHAPE;
   hipStream_t st = (hipStream_t)stream;
   if (g.d == 64)
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);

@@ -51,6 +51,34 @@ __device__ __forceinline__ uint4 buf_load16(rsrc_t r, uint32_t voff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0));
 }
 
+// Direct global -> LDS load (buffer_load_dwordx4 ... lds): lane i's 16 bytes
+// from byte offset voff land at byte 16*i of the wave's 1 KB LDS window that
+// starts at lds (wave-uniform); offsets past the resource range write zeros
+// (both checked on gfx950). Completion is waited for with wait_vmem(). The
+// compiler makes LDS reads wait for such loads unless it can tell the two
+// apart, so the stages they fill are separate __shared__ arrays, each
+// addressed by name.
+__device__ __forceinline__ void buf_load16_lds(rsrc_t r, const void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)const_cast<void*>(lds), 16, (int)voff, 0, 0, 0);
+}
+// Same with 4 bytes per lane (lane i lands at byte 4*i of a 256-byte window).
+__device__ __forceinline__ void buf_load4_lds(rsrc_t r, const void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      r, (__attribute__((address_space(3))) void*)const_cast<void*>(lds), 4, (int)voff, 0, 0, 0);
+}
+// s_waitcnt vmcnt(0), leaving the other counters alone (gfx9 encoding: vmcnt
+// bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt lgkmcnt(0) alone (vmcnt 63, expcnt 7), then s_barrier: a workgroup
+// barrier that orders LDS accesses but lets global loads stay in flight.
+__device__ __forceinline__ void barrier_lds_only() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // 16-bit halves of two words: (hi.lo16 << 16 | lo.lo16) and (hi.hi16 << 16 | lo.hi16).
 __device__ __forceinline__ uint32_t pack_lo16(uint32_t lo, uint32_t hi) {
   return __builtin_amdgcn_perm(hi, lo, 0x05040100u);
@@ -130,6 +158,28 @@ __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32,
 // exp2 on the hardware transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+
+// Workgroup order: heads (units) in groups of kUnitGroup, each group's tiles
+// ordered by level (slowest), then document, then unit (fastest). Consecutive
+// workgroups go to consecutive XCDs, so with eight units per group each XCD
+// works on one head at a time and its L2 serves every workgroup of that head.
+constexpr int kUnitGroup = 8;
+struct TileId {
+  int lvl, doc, unit;
+};
+__device__ __forceinline__ TileId decode_tile(int bid, int nslots, int ndoc, int units) {
+  const int per_group = nslots * ndoc * kUnitGroup;
+  const int gi = bid / per_group;
+  const int r = bid - gi * per_group;
+  const int ug = min(kUnitGroup, units - gi * kUnitGroup);
+  const int per_level = ndoc * ug;
+  TileId t;
+  t.lvl = r / per_level;
+  const int rem = r - t.lvl * per_level;
+  t.doc = rem / ug;
+  t.unit = gi * kUnitGroup + (rem - t.doc * ug);
+  return t;
+}
 }  // namespace uly
 
 // ---------------------------------------------------------------- host side
