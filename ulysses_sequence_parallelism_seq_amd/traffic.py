@@ -83,12 +83,13 @@ def read_traffic(path: str):
                 rec[(parts[0], parts[1])] = dict(p.split("=") for p in parts[2:])
     if rec.get("sha") != sources_sha256():
         return None
-    copy = next(v for (kind, _), v in rec.items() if kind == "copy")
+    entries = [(k, v) for k, v in rec.items() if isinstance(k, tuple)]
+    copy = next(v for (kind, _), v in entries if kind == "copy")
     copy_kib = float(copy["bytes"]) / 1024.0  # the copy reads this many KiB and writes as many
     f_scale = copy_kib / float(copy["fetch_kib"])
     w_scale = copy_kib / float(copy["write_kib"])
     total = 0.0
-    for (kind, _), v in rec.items():
+    for (kind, _), v in entries:
         if kind == "kernel":
             total += float(v["fetch_kib"]) * f_scale + float(v["write_kib"]) * w_scale
     return {"bytes": total * 1024.0, "fetch_scale": f_scale, "write_scale": w_scale}
