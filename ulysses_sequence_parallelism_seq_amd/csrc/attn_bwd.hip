@@ -112,51 +112,20 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
   }
 }
 
-// ----------------------------------------------------------- shared tile staging
-// A tile of kRows tokens of two [token][d] tensors, staged global -> registers
-// -> LDS (RowTile layout) by kNT threads. Thread tid moves the 16-byte chunks
-// id = tid + j*kNT (token id/(D/8), column chunk id%(D/8)). Loads go
-// through buffer resources ending at the document end: rows past it read as
-// zero and the per-thread offsets are the same for every tile.
-template <int D, int kRows, int kNT = kThreads>
-struct PairTile {
-  using L = RowTile<D>;
-  static constexpr int RS = L::RS;                  // LDS row stride (bf16)
-  static constexpr int CH = kRows * D / 8 / kNT;    // chunks per thread per tensor
-  static constexpr int kRowStep = kNT / (D / 8);    // tokens between a thread's chunks
-  uint4 a[CH];
-  uint4 b[CH];
-
-  __device__ __forceinline__ void load(rsrc_t ra, rsrc_t rb, uint32_t off0, uint32_t row_bytes) {
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const uint32_t off = off0 + (uint32_t)(j * kRowStep) * row_bytes;
-      a[j] = buf_load16(ra, off);
-      b[j] = buf_load16(rb, off);
-    }
-  }
-  __device__ __forceinline__ void store(bf16* sa, bf16* sb, int tid) const {
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int at = L::off(tid / (D / 8) + j * kRowStep, (tid % (D / 8)) * 8);
-      *reinterpret_cast<uint4*>(sa + at) = a[j];
-      *reinterpret_cast<uint4*>(sb + at) = b[j];
-    }
-  }
-};
-
 // --------------------------------------------------------------------- dq kernel
 constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
 constexpr int kDqBK = 64;   // keys per tile
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
-  using T = PairTile<D, kDqBK>;
-  constexpr int RS = T::RS;
+  using L = RowTile<D>;
   constexpr int KK = D / 16, CB = D / 32;
-  constexpr int TILE = kDqBK * RS;   // bf16 elements of one staged tensor
-  constexpr int STAGE = 2 * TILE;    // K then V
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * STAGE];
+  constexpr int TILE = kDqBK * L::RS;  // bf16 elements of one staged tensor
+  // K and V of even tiles, then of odd tiles (named stages: see TileDma)
+  __shared__ __attribute__((aligned(16))) bf16 k0s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 v0s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 k1s[TILE];
+  __shared__ __attribute__((aligned(16))) bf16 v1s[TILE];
 
   const TileId tid_ = decode_tile(blockIdx.x, a.nslots, a.ndoc, a.units);
   const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
@@ -199,21 +168,24 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) dqacc[cb][i] = 0.f;
 
-  const uint32_t off0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
   auto rsrc_at = [&](const bf16* p, int kt0) {
     return make_rsrc(p + base + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
   };
-  T tile;
-  tile.load(rsrc_at(a.k, s), rsrc_at(a.v, s), off0, row_bytes);
-  tile.store(smem, smem + TILE, tid);
+  // K/V tiles by direct-to-LDS loads: tile t+1 goes out before the math of
+  // tile t and is waited for before its barrier
+  TileDma<D, kDqBK, kThreads / 64> dma;
+  dma.init(w, lane, row_bytes);
+  dma.issue(rsrc_at(a.k, s), k0s);
+  dma.issue(rsrc_at(a.v, s), v0s);
+  wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](int t, const bf16* ks, const bf16* vs, const bf16* kn, const bf16* vn) {
     const int kt0 = s + t * kDqBK;
-    const bf16* ks = smem + (t & 1) * STAGE;
-    const bf16* vs = ks + TILE;
-    const bool more = t + 1 < ntiles;
-    if (more) tile.load(rsrc_at(a.k, kt0 + kDqBK), rsrc_at(a.v, kt0 + kDqBK), off0, row_bytes);
+    if (t + 1 < ntiles) {
+      dma.issue(rsrc_at(a.k, kt0 + kDqBK), kn);
+      dma.issue(rsrc_at(a.v, kt0 + kDqBK), vn);
+    }
 
     if (!a.causal || kt0 <= q0 + 32 * w + 31) {
       const bool need_mask = (a.causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
@@ -227,7 +199,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
         for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const int off = T::L::off(blk * 32 + l32, 16 * kk + 8 * half);
+          const int off = L::off(blk * 32 + l32, 16 * kk + 8 * half);
           const uint4 ka = *reinterpret_cast<const uint4*>(ks + off);
           const uint4 va = *reinterpret_cast<const uint4*>(vs + off);
           sacc = mfma32(as_bf16x8(ka), as_bf16x8(qreg[kk]), sacc);
@@ -260,11 +232,12 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
       }
     }
 
-    if (more) {
-      bf16* nk = smem + ((t + 1) & 1) * STAGE;
-      tile.store(nk, nk + TILE, tid);
-    }
+    wait_vmem();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, k0s, v0s, k1s, v1s);
+    if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
   }
 
   if (qvalid) {

@@ -22,14 +22,16 @@
 //     operand V^T comes from the row-major V tile through gfx950's
 //     transposing LDS reads. The MFMA k index is mapped to keys so that each
 //     lane's own P values form its B operand (no data movement between
-//     lanes). The O^T
-//     accumulator has one query per lane, so the rescale by the running-max
-//     correction is a per-lane scalar.
-//   * K/V tiles of 64 keys are staged in LDS (both row-major, padded rows),
-//     double-buffered: the global loads of tile t+1 are issued before the
-//     math of tile t and written to the other buffer after it, one barrier
-//     per tile. Loads go through buffer resources ending at the document
-//     end (hardware zero-fill past it; per-thread offsets fixed per kernel).
+//     lanes). The O^T accumulator has one query per lane, so the rescale by
+//     the running-max correction is a per-lane scalar.
+//   * K/V tiles of 64 keys are staged in LDS (row-major, swizzled 16-byte
+//     chunks), double-buffered: direct-to-LDS loads of tile t+1 are issued
+//     before the math of tile t and waited for before its barrier, one
+//     barrier per tile. The two stages are separate arrays addressed by
+//     name (the loop is unrolled by two), so the compiler can tell the
+//     stage being loaded from the one being read. Loads go through buffer
+//     resources ending at the document end (zeros past it; per-lane offsets
+//     fixed per kernel).
 //   * Documents: a query tile never straddles a document; its keys run from
 //     the document start to the tile's last query (causal) or the document
 //     end. Only the tiles that cross the diagonal or the document end are
@@ -54,10 +56,8 @@ constexpr int kThreads = 512;  // 8 waves sharing each K/V tile
 
 template <int D>
 struct FwdSmem {
-  using L = RowTile<D>;  // K and V tiles, row-major (swizzled for d = 128)
-  static constexpr int K_ELEMS = kBK * L::RS;
-  static constexpr int V_ELEMS = kBK * L::RS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
+  using L = RowTile<D>;  // K and V tiles, row-major, swizzled chunks
+  static constexpr int TILE = kBK * L::RS;
 };
 
 struct FwdArgs {
@@ -76,41 +76,6 @@ struct FwdArgs {
   float sl2;  // log2(e) / sqrt(d)
 };
 
-// Global -> register staging of one K/V tile: thread tid moves the 16-byte
-// chunks id = tid + j*kThreads (token id/(D/8), column chunk id%(D/8)) of K
-// and of V. Loads go through buffer resources whose range ends at the
-// document end, so rows past it read as zero and the per-thread offsets are
-// the same for every tile.
-template <int D>
-struct TileRegs {
-  static constexpr int KCH = kBK * D / 8 / kThreads;  // 16-byte chunks per thread per tensor
-  static constexpr int kRowStep = kThreads / (D / 8);  // tokens between a thread's chunks
-  uint4 kr[KCH];
-  uint4 vr[KCH];
-};
-
-template <int D>
-__device__ __forceinline__ void load_tile(TileRegs<D>& r, uint32_t off0, rsrc_t kr, rsrc_t vr,
-                                          uint32_t row_bytes) {
-#pragma unroll
-  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
-    const uint32_t off = off0 + (uint32_t)(j * TileRegs<D>::kRowStep) * row_bytes;
-    r.kr[j] = buf_load16(kr, off);
-    r.vr[j] = buf_load16(vr, off);
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void store_tile(const TileRegs<D>& r, bf16* ks, bf16* vs, int tid) {
-  using L = RowTile<D>;
-#pragma unroll
-  for (int j = 0; j < TileRegs<D>::KCH; ++j) {
-    const int at = L::off(tid / (D / 8) + j * TileRegs<D>::kRowStep, (tid % (D / 8)) * 8);
-    *reinterpret_cast<uint4*>(ks + at) = r.kr[j];
-    *reinterpret_cast<uint4*>(vs + at) = r.vr[j];
-  }
-}
-
 // Lazy rescale: the running max used in the exponentials only moves when a
 // row's new maximum exceeds it by more than 8 (log2 units). The O accumulator
 // is then rescaled rarely, and P = exp2(x - m) stays below 2^8, which fp32
@@ -123,7 +88,11 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   using S = FwdSmem<D>;
   constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
   constexpr int CB = D / 32;  // 32-wide column blocks of O^T
-  __shared__ __attribute__((aligned(16))) bf16 smem[2 * S::STAGE];
+  // K and V of even tiles, then of odd tiles
+  __shared__ __attribute__((aligned(16))) bf16 k0s[S::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 v0s[S::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 k1s[S::TILE];
+  __shared__ __attribute__((aligned(16))) bf16 v1s[S::TILE];
 
   // ---- which tile
   const TileId tid_ = decode_tile(blockIdx.x, a.nq_slots, a.ndoc, a.units);
@@ -169,21 +138,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
 
-  const uint32_t off0 = (uint32_t)(tid / (D / 8)) * row_bytes + (uint32_t)(tid % (D / 8)) * 16u;
-  TileRegs<D> tr;
+  TileDma<D, kBK, kThreads / 64> dma;
+  dma.init(w, lane, row_bytes);
   auto rsrc_at = [&](const bf16* p, int kt0) {
     return make_rsrc(p + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
   };
-  load_tile<D>(tr, off0, rsrc_at(kb, s), rsrc_at(vb, s), row_bytes);
-  store_tile<D>(tr, smem, smem + S::K_ELEMS, tid);
+  dma.issue(rsrc_at(kb, s), k0s);
+  dma.issue(rsrc_at(vb, s), v0s);
+  wait_vmem();
   __syncthreads();
 
-  for (int t = 0; t < ntiles; ++t) {
+  auto step = [&](int t, const bf16* ks, const bf16* vs, const bf16* kn, const bf16* vn) {
     const int kt0 = s + t * kBK;
-    const bf16* ks = smem + (t & 1) * S::STAGE;
-    const bf16* vs = ks + S::K_ELEMS;
-    const bool more = t + 1 < ntiles;
-    if (more) load_tile<D>(tr, off0, rsrc_at(kb, kt0 + kBK), rsrc_at(vb, kt0 + kBK), row_bytes);
+    if (t + 1 < ntiles) {
+      dma.issue(rsrc_at(kb, kt0 + kBK), kn);
+      dma.issue(rsrc_at(vb, kt0 + kBK), vn);
+    }
 
     const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
     if (wave_active) {
@@ -260,8 +230,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
           oacc[cb] = mfma32(a_from_rows<D>(vs, 16 * st, 32 * cb, lane), as_bf16x8(pb[st]), oacc[cb]);
     }
 
-    if (more) store_tile<D>(tr, smem + ((t + 1) & 1) * S::STAGE, smem + ((t + 1) & 1) * S::STAGE + S::K_ELEMS, tid);
+    wait_vmem();
     __syncthreads();
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, k0s, v0s, k1s, v1s);
+    if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
   }
 
   // ---- normalise and write O (one query per lane, 4 consecutive columns per store) and lse

@@ -136,6 +136,38 @@ struct RowTile {
   }
 };
 
+// Global -> LDS staging of a kRows-token tile of one [token][d] tensor with
+// direct-to-LDS loads, by kWaves waves: wave w fills rows
+// [w * kRows / kWaves, (w + 1) * kRows / kWaves), 1 KB (64 / (D/8) whole rows)
+// per instruction. Lane i lands on physical chunk i % (D/8) of its row, so it
+// fetches the logical chunk that the RowTile swizzle keeps there. The buffer
+// range ends at the document end: rows past it are written as zeros.
+template <int D, int kRows, int kWaves>
+struct TileDma {
+  static constexpr int CHUNKS = D / 8;
+  static constexpr int ROWS_PER_OP = 64 / CHUNKS;
+  static constexpr int ROWS_PER_WAVE = kRows / kWaves;
+  static constexpr int OPS = ROWS_PER_WAVE / ROWS_PER_OP;
+  static_assert(OPS >= 1 && OPS * ROWS_PER_OP == ROWS_PER_WAVE, "a wave fills whole 1 KB windows");
+  uint32_t voff[OPS];
+  int lds_off[OPS];
+
+  __device__ __forceinline__ void init(int w, int lane, uint32_t row_bytes) {
+#pragma unroll
+    for (int j = 0; j < OPS; ++j) {
+      const int row0 = ROWS_PER_WAVE * w + ROWS_PER_OP * j;
+      const int r = row0 + lane / CHUNKS;
+      const int c = (lane % CHUNKS) ^ RowTile<D>::chunk_key(r);
+      voff[j] = (uint32_t)r * row_bytes + (uint32_t)c * 16u;
+      lds_off[j] = row0 * D;
+    }
+  }
+  __device__ __forceinline__ void issue(rsrc_t rs, const bf16* tile) const {
+#pragma unroll
+    for (int j = 0; j < OPS; ++j) buf_load16_lds(rs, tile + lds_off[j], voff[j]);
+  }
+};
+
 // MFMA A operand (rows = 32 columns c0 .. c0+31 of a [token][d] LDS tile in
 // the RowTile layout; k = 16 tokens from t0) read with two transposing
 // reads. Lane l (h = l / 32) receives column c0 + l % 32 of tokens
