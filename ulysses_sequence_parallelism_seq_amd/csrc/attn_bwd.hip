@@ -12,20 +12,21 @@
 //
 // Work split (no atomics, so every output is written by exactly one lane and
 // results are bit-reproducible):
-//   * dq kernel, query-stationary: a workgroup owns 128 queries (32 per
+//   * dq kernel, query-stationary: a workgroup owns 256 queries (32 per
 //     wave, Q and dO resident in registers as MFMA B operands) and walks the
-//     64-key K/V tiles of its document (double-buffered in LDS). Per tile: S^T = K Q^T and
+//     64-key K/V tiles of its document (double-buffered in LDS, filled by
+//     direct-to-LDS loads). Per tile: S^T = K Q^T and
 //     dP^T = V dO^T (lane = query, so lse_i and D_i are per-lane scalars),
 //     dS^T in registers, then dQ^T += K^T dS^T (K^T read from the row-major
 //     K tile with gfx950's transposing LDS reads).
-//   * dkdv kernel, key-stationary: a workgroup of 8 waves owns 128 keys (K
-//     and V resident as B operands, each 32-key group shared by two waves)
-//     and walks 64-query tiles (Q, dO, lse, D double-buffered in LDS) from the
-//     document end down to its first key (causal). Per tile: S = Q K^T and dP = dO V^T
-//     (lane = key), then dV^T += dO^T P and dK^T += Q^T dS with the A
-//     operands read transposed from the row-major Q and dO tiles; the
-//     accumulators hold one key per lane, so the final stores are 4
-//     consecutive columns per lane.
+//   * dkdv kernel, key-stationary: a workgroup of 8 waves owns 128 keys and
+//     walks 64-query tiles (Q, dO, lse, D in three LDS stages) from the
+//     document end down to its first key (causal). Producer waves compute
+//     S = Q K^T, dP = dO V^T (lane = key; K and V resident as B operands),
+//     P and dS; consumer waves, one tile behind, accumulate dV^T += dO^T P
+//     and dK^T += Q^T dS with the A operands read transposed from the
+//     row-major Q and dO tiles; the accumulators hold one key per lane, so
+//     the final stores are 4 consecutive columns per lane.
 // The MFMA k index of a 16-wide step maps to tokens the same way as in the
 // forward kernel, so P and dS feed the MFMA straight from the accumulators.
 
@@ -113,11 +114,12 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
 }
 
 // --------------------------------------------------------------------- dq kernel
-constexpr int kDqBQ = 128;  // queries per workgroup (32 per wave)
+constexpr int kDqBQ = 256;       // queries per workgroup (32 per wave)
+constexpr int kDqThreads = 512;  // 8 waves sharing each K/V tile, one workgroup per CU
 constexpr int kDqBK = 64;   // keys per tile
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
+__global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) {
   using L = RowTile<D>;
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int TILE = kDqBK * L::RS;  // bf16 elements of one staged tensor
@@ -173,7 +175,7 @@ __global__ __launch_bounds__(kThreads, 2) void attn_dq_bf16_kernel(BwdArgs a) {
   };
   // K/V tiles by direct-to-LDS loads: tile t+1 goes out before the math of
   // tile t and is waited for before its barrier
-  TileDma<D, kDqBK, kThreads / 64> dma;
+  TileDma<D, kDqBK, kDqThreads / 64> dma;
   dma.init(w, lane, row_bytes);
   dma.issue(rsrc_at(a.k, s), k0s);
   dma.issue(rsrc_at(a.v, s), v0s);
@@ -585,12 +587,12 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
     hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
                        lse, delta, a.lse2, g.N, g.Hl, rows);
     hipLaunchKernelGGL(attn_dkdv_bf16_kernel<64>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL(attn_dq_bf16_kernel<64>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, aq);
+    hipLaunchKernelGGL(attn_dq_bf16_kernel<64>, dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   } else {
     hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
                        lse, delta, a.lse2, g.N, g.Hl, rows);
     hipLaunchKernelGGL(attn_dkdv_bf16_kernel<128>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL(attn_dq_bf16_kernel<128>, dim3((unsigned)qblocks), dim3(kThreads), 0, st, aq);
+    hipLaunchKernelGGL(attn_dq_bf16_kernel<128>, dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   }
   return launch_status();
 }
