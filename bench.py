@@ -13,7 +13,10 @@ timed with HIP events on the stream it runs on.
 
 value = causal attention FLOPs counted as 14 * d * pairs (4 d forward, 10 d
 backward; pairs = sum over documents of L (L + 1) / 2 per row and head)
-divided by the whole step's time, in TFLOP/s.
+divided by the whole step's time, in TFLOP/s. The config also carries the
+same time counted as 12 * d * pairs (no recompute of S counted), the permute
+bandwidth next to a plain device-to-device copy of one tensor of the same
+size timed in the same run, and the per-call averages.
 
 Prints one JSON line. --gpus above 1 exits: this build measures one GPU.
 """
@@ -135,10 +138,17 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
     if M2 > M:
         M, t = M2, run(M2)
     flops = 14 * w.d * (M * (M + 1) // 2)
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), cpu_model)
+    except OSError:
+        pass
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
+        "cpu_model": cpu_model,
         "kind": "oracle",
         "sample": f"float64 oracle fwd+bwd of one head, causal prefix of {M} of the {w.N} tokens "
                   f"({t:.1f} s; FLOPs counted as 14*d*pairs like the GPU value)",
@@ -195,6 +205,15 @@ def main():
     elapsed = time.perf_counter() - t0
     avg, counts = timer.averages()
 
+    # reference for the permute: a plain device-to-device copy of one tensor of the same size
+    copy_dst = torch.empty_like(seq_in[0])
+    copy_timer = Timer(stream)
+    for _ in range(5):
+        copy_timer.run("copy", lambda: copy_dst.copy_(seq_in[0]))
+    torch.cuda.synchronize()
+    copy_ms = copy_timer.averages()[0]["copy"]
+    del copy_dst
+
     ms_per_step = elapsed * 1e3 / args.steps
     pairs = causal_pairs(w) * w.sp * w.B * w.Hl  # all virtual ranks, batch rows, local heads
     flops_step = 14 * w.d * pairs
@@ -234,6 +253,8 @@ def main():
             "permute_ms": round(statistics.mean([avg["seq_to_head"], avg["head_to_seq"]]), 4),
             "permute_gbs": round(permute_gbs, 1),
             "permute_pct_of_hbm_peak": round(100 * permute_gbs / PEAK_HBM_GBS, 1),
+            "d2d_copy_gbs": round(2 * tensor_bytes / (copy_ms * 1e-3) / 1e9, 1),
+            "value_12d_no_recompute": round(12 * w.d * pairs / (ms_per_step * 1e-3) / 1e12, 2),
             "flops_per_step": flops_step,
             "calls_timed": counts,
         },
