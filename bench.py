@@ -65,6 +65,23 @@ def make_inputs(w: workloads.Workload, dev):
     return out
 
 
+def make_buffers(w: workloads.Workload, dev):
+    """Inputs (sequence shards) and every buffer one step writes, allocated once."""
+    seq_in = make_inputs(w, dev)
+    head_shape = (w.sp, w.B, w.N, w.Hl, w.d)
+    dt = workloads.torch_dtype(w.dtype)
+    return {
+        "seq_in": seq_in,
+        "head_in": [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(4)],
+        "head_out": [torch.empty(head_shape, dtype=dt, device=dev),
+                     torch.empty((w.sp, w.B, w.Hl, w.N), dtype=torch.float32, device=dev)]
+                    + [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(3)],
+        "seq_out": [torch.empty_like(seq_in[0]) for _ in range(4)],
+        "ws": torch.empty(uly.ulysses_attn_bwd_workspace_bytes(w.sp, w.B, w.N, w.Hl, w.d, dt),
+                          dtype=torch.uint8, device=dev),
+    }
+
+
 class Timer:
     """HIP-event timing of each named call over the timed steps."""
 
@@ -177,19 +194,8 @@ def main():
     cu = workloads.workload_cu_seqlens(w)
     packing = None if cu is None else uly.DocPacking(cu, w.N, dev)
 
-    seq_in = make_inputs(w, dev)
-    head_shape = (w.sp, w.B, w.N, w.Hl, w.d)
-    dt = workloads.torch_dtype(w.dtype)
-    bufs = {
-        "seq_in": seq_in,
-        "head_in": [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(4)],
-        "head_out": [torch.empty(head_shape, dtype=dt, device=dev),
-                     torch.empty((w.sp, w.B, w.Hl, w.N), dtype=torch.float32, device=dev)]
-                    + [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(3)],
-        "seq_out": [torch.empty_like(seq_in[0]) for _ in range(4)],
-        "ws": torch.empty(uly.ulysses_attn_bwd_workspace_bytes(w.sp, w.B, w.N, w.Hl, w.d, dt),
-                          dtype=torch.uint8, device=dev),
-    }
+    bufs = make_buffers(w, dev)
+    seq_in = bufs["seq_in"]
     stream = torch.cuda.current_stream(dev)
 
     for _ in range(args.warmup):

@@ -156,3 +156,53 @@ def test_fullsize_permute(name):
     rows = torch.from_numpy((np.arange(w.sp)[:, None] * w.Ns + idx[None, :]).reshape(-1)).to(dev)
     got = head.view(torch.int16).index_select(2, rows).cpu().numpy()
     assert np.array_equal(got, want)
+
+
+def test_bench_step_long_sampled():
+    """The exact step bench.py times on the long workload (q, k, v through
+    seq_to_head, one attention call over all 8 stacked virtual-rank shares,
+    head_to_seq back, the backward likewise), checked on sampled outputs of
+    three heads held by different virtual ranks against the oracle run on the
+    unsharded full-H tensors."""
+    import bench
+
+    w = workloads.WORKLOADS["long"]
+    say("bench step, sampled", w)
+    dev = device()
+    bufs = bench.make_buffers(w, dev)
+    bench.step(w, bufs, None)
+    torch.cuda.synchronize()
+    q, k, v, do = bufs["seq_in"]
+    outs = dict(zip(("O", "dQ", "dK", "dV"), bufs["seq_out"]))
+    lse = bufs["head_out"][1]
+
+    def full_head(x, h):  # [sp][B][Ns][H][d] -> the whole sequence of batch row 0, head h: [N][d]
+        return x[:, 0, :, h].reshape(w.N, w.d).cpu()
+
+    rng = np.random.default_rng(w.seed)
+    rows = _sample_rows([(0, w.N)], rng, 12)
+    cols = _end_cols([(0, w.N)], 32)
+    got = {n: [] for n in outs}
+    want = {n: [] for n in outs}
+    lse_err = 0.0
+    for h in (0, 13, 31):  # virtual ranks 0, 3 and 7
+        qh, kh, vh, doh = (full_head(x, h) for x in (q, k, v, do))
+        O_r, L_r = oracle.attn_fwd_rows(qh, kh, vh, rows)
+        got["O"].append(f64(full_head(outs["O"], h))[rows])
+        want["O"].append(O_r)
+        lse_err = max(lse_err, float(np.abs(f64(lse[h // w.Hl, 0, h % w.Hl].cpu())[rows] - L_r).max()))
+        got["dQ"].append(f64(full_head(outs["dQ"], h))[rows])
+        want["dQ"].append(oracle.attn_bwd_dq_rows(qh, kh, vh, doh, rows))
+        dk_c, dv_c = oracle.attn_bwd_dkdv_cols(qh, kh, vh, doh, cols)
+        got["dK"].append(f64(full_head(outs["dK"], h))[cols])
+        want["dK"].append(dk_c)
+        got["dV"].append(f64(full_head(outs["dV"], h))[cols])
+        want["dV"].append(dv_c)
+    del bufs
+    torch.cuda.empty_cache()
+    for n in outs:
+        tol = TOL_BF16_O if n == "O" else TOL_BF16_GRAD
+        err = assert_rel(np.stack(got[n]), np.stack(want[n]), tol, f"bench step {n}")
+        say(f"bench step {n} rel err {err:.3e}")
+    say(f"bench step lse max abs err {lse_err:.3e}")
+    assert lse_err < 1e-3
