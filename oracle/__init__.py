@@ -11,6 +11,9 @@ Contents:
   attention  exact softmax attention (causal or not, packed documents kept
              apart) forward with its log-sum-exp, and the analytic backward,
              in float64 with whole-row normalisation.
+  ring       the ring-attention variant: blockwise attention of each rank's
+             query chunk against key/value chunks passed around a ring,
+             partial results merged by their log-sum-exp; its backward.
 
 Every function here is pinned by tests that do not call it twice: closed
 forms, finite differences, brute-force loops, an independent library
@@ -26,3 +29,4 @@ from .attention import (  # noqa: F401
     attn_bwd_dkdv_cols,
     doc_ids,
 )
+from .ring import ring_fwd, ring_bwd, ring_chunk, block_mode, block_attn, merge, stitch, stitch_lse  # noqa: F401
