@@ -18,6 +18,12 @@ same time counted as 12 * d * pairs (no recompute of S counted), the permute
 bandwidth next to a plain device-to-device copy of one tensor of the same
 size timed in the same run, and the per-call averages.
 
+With --variant ring the step is ring attention instead (the other
+sequence-parallel mode): the same q, k, v, dO sequence shards, no layout
+change; sp forward ring steps (each rank's queries against the key/value
+chunk passed to it, partial results merged by log-sum-exp), the D pre-pass,
+then sp backward ring steps. Same FLOP count, same value definition.
+
 Prints one JSON line. --gpus above 1 exits: this build measures one GPU.
 """
 
@@ -125,6 +131,38 @@ def step(w, bufs, packing, timer=None):
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dv, out=dvs))
 
 
+def make_ring_buffers(w: workloads.Workload, dev):
+    """Ring variant: the sequence shards are the ring's chunks; fp32 running sums and bf16 outputs."""
+    seq_in = make_inputs(w, dev)
+    shape = workloads.seq_shard_shape(w)
+    dt = workloads.torch_dtype(w.dtype)
+    f32 = lambda: torch.empty(shape, dtype=torch.float32, device=dev)  # noqa: E731
+    return {
+        "seq_in": seq_in,
+        "o": torch.empty(shape, dtype=dt, device=dev),
+        "o_acc": f32(),
+        "lse": torch.empty((w.sp, w.B, w.H, w.Ns), dtype=torch.float32, device=dev),
+        "grads": [torch.empty(shape, dtype=dt, device=dev) for _ in range(3)],
+        "accs": [f32() for _ in range(3)],
+        "ws": torch.empty(uly.ulysses_ring_attn_bwd_workspace_bytes(w.sp, w.B, w.Ns, w.H, w.d),
+                          dtype=torch.uint8, device=dev),
+    }
+
+
+def ring_step(w, bufs, timer=None):
+    run = timer.run if timer else (lambda name, fn: fn())
+    q, k, v, do = bufs["seq_in"]
+    o, o_acc, lse, ws = bufs["o"], bufs["o_acc"], bufs["lse"], bufs["ws"]
+    dq, dk, dv = bufs["grads"]
+    dqa, dka, dva = bufs["accs"]
+    for i in range(w.sp):
+        run("ring_fwd_step", lambda: uly.ulysses_ring_attn_fwd_step(q, k, v, i, w.causal, o, o_acc, lse))
+    run("ring_bwd_prepare", lambda: uly.ulysses_ring_attn_bwd_prepare(o, do, lse, ws))
+    for i in range(w.sp):
+        run("ring_bwd_step", lambda: uly.ulysses_ring_attn_bwd_step(q, k, v, do, lse, ws, i, w.causal,
+                                                                     dqa, dka, dva, dq, dk, dv))
+
+
 def cpu_baseline(w: workloads.Workload, target_s: float):
     """The float64 oracle, fwd + bwd, on the causal prefix of one head (bounded sample)."""
     import oracle
@@ -180,6 +218,7 @@ def main():
     ap.add_argument("--workload", default="long", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--variant", default="ulysses", choices=["ulysses", "ring"])
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -192,6 +231,11 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cu = workloads.workload_cu_seqlens(w)
+    if args.variant == "ring":
+        if cu is not None or w.dtype != "bf16":
+            print("the ring variant runs bf16 workloads with one document per row", file=sys.stderr)
+            sys.exit(2)
+        return ring_main(args, w, dev)
     packing = None if cu is None else uly.DocPacking(cu, w.N, dev)
 
     bufs = make_buffers(w, dev)
@@ -274,6 +318,70 @@ def main():
             "traffic": None if traffic is None else round(traffic["bytes"]),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "compulsory_bytes": min_bwd_bytes,
+            "flops_per_launch": 10 * w.d * pairs,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def ring_main(args, w, dev):
+    bufs = make_ring_buffers(w, dev)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        ring_step(w, bufs)
+    torch.cuda.synchronize()
+    timer = Timer(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ring_step(w, bufs, timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg, counts = timer.averages()
+    ms_per_step = elapsed * 1e3 / args.steps
+    pairs = causal_pairs(w) * w.B * w.H  # the whole sequence, every head
+    flops_step = 14 * w.d * pairs
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    fwd_ms = w.sp * avg["ring_fwd_step"]
+    bwd_ms = avg["ring_bwd_prepare"] + w.sp * avg["ring_bwd_step"]
+    bwd_tflops = 10 * w.d * pairs / (bwd_ms * 1e-3) / 1e12
+    result = {
+        "metric": "ring attention fwd+bwd TFLOP/s per GPU (% bf16 MFMA peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) q/k/v/dO on the device)",
+        "config": {
+            "workload": f"{w.name} as a ring: B={w.B} N={w.N} H={w.H} sp={w.sp} chunks of {w.Ns} tokens "
+                        f"(all {w.sp} virtual ranks on one GPU) d={w.d} {w.dtype} causal={w.causal}",
+            "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "ring_fwd_ms": round(fwd_ms, 3),
+            "ring_bwd_ms": round(bwd_ms, 3),
+            "ring_fwd_step_ms": round(avg["ring_fwd_step"], 3),
+            "ring_bwd_step_ms": round(avg["ring_bwd_step"], 3),
+            "ring_bwd_prepare_ms": round(avg["ring_bwd_prepare"], 3),
+            "ring_fwd_tflops": round(4 * w.d * pairs / (fwd_ms * 1e-3) / 1e12, 1),
+            "ring_bwd_tflops": round(bwd_tflops, 1),
+            "flops_per_step": flops_step,
+            "calls_timed": counts,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"ring backward (D pre-pass + {w.sp} ring steps of dK/dV + dQ kernels)",
+            "achieved": round(bwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
             "flops_per_launch": 10 * w.d * pairs,
         },
         "cpu_baseline": None,

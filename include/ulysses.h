@@ -126,6 +126,77 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len,
                      int sp, int B, int N, int Hl, int d, int causal, int dtype, void* stream);
 
+/*
+ * Ring attention, the other sequence-parallel mode (ColossalAI docs,
+ * "Sequence Parallelism": sequence_parallelism_mode="ring_attn", related
+ * paper "Ring Attention with Blockwise Transformers"; the closing comparison
+ * notes it has no head-count condition). sp virtual ranks on one device:
+ * rank r keeps token chunk r (Ns = N/sp tokens) of all H heads. At ring step
+ * i = 0 .. sp-1 rank r holds key/value chunk j = (r - i) mod sp (passed one
+ * rank along the ring per step), attends its queries to that block and
+ * merges the block's partial result with its running one by log-sum-exp:
+ *   lse' = log(exp(lse) + exp(lse_blk)),
+ *   O'   = exp(lse - lse') O + exp(lse_blk - lse') O_blk.
+ * Block mask, in global positions: causal -> j < r every key, j == r the
+ * causal diagonal, j > r none (the rank idles); causal == 0 -> every key.
+ * After sp steps O and lse are softmax attention over the whole sequence.
+ * Only ULY_BF16 is supported; d is 64 or 128.
+ *
+ * Forward step i:
+ *   q, k, v  [sp][B][Ns][H][d] bf16, the sequence-sharded layout (k, v of
+ *            every chunk; the step picks chunk j for rank r)
+ *   o_acc    [sp][B][Ns][H][d] float: running normalised output; read at
+ *            step i > 0, written at every step
+ *   lse      [sp][B][H][Ns] float: running log-sum-exp (natural log); read
+ *            at step i > 0, written at every step
+ *   o        [sp][B][Ns][H][d] bf16: rank r's rows are written at its last
+ *            step (i == r when causal, i == sp-1 otherwise)
+ * Steps run in order 0, 1, .., sp-1 (step 0 ignores o_acc and lse on entry).
+ * Errors: ULY_EINVAL (null pointer, size <= 0, step outside [0, sp)),
+ * ULY_EUNSUPPORTED (dtype, d), ULY_ESHAPE, ULY_EHIP.
+ */
+int ulysses_ring_attn_fwd_step(const void* q, const void* k, const void* v, void* o, float* o_acc,
+                               float* lse, int step, int sp, int B, int Ns, int H, int d, int causal,
+                               int dtype, void* stream);
+
+/*
+ * Bytes of workspace the ring backward needs: two floats per (rank, batch
+ * row, head, token) (D = rowsum(dO * O) and lse in log2 units). Returns 0 for
+ * invalid arguments.
+ */
+size_t ulysses_ring_attn_bwd_workspace_bytes(int sp, int B, int Ns, int H, int d, int dtype);
+
+/*
+ * Before the backward steps: D = rowsum(dO * O) and lse * log2(e) of every
+ * query row into the workspace, from the forward's final o and lse.
+ *   o, dout [sp][B][Ns][H][d] bf16; lse [sp][B][H][Ns] float.
+ * Errors: as ulysses_ring_attn_fwd_step, plus ULY_EWORKSPACE.
+ */
+int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, const float* lse, void* workspace,
+                                  size_t workspace_bytes, int sp, int B, int Ns, int H, int d,
+                                  int dtype, void* stream);
+
+/*
+ * Backward step i (the adjoint of the forward's block of rank r and chunk
+ * j = (r - i) mod sp). With P = exp(S - lse) of the block, dP = dO V_j^T and
+ * dS = P * (dP - D):
+ *   dQ_r += scale dS K_j,  dK_j += scale dS^T Q_r,  dV_j += P^T dO_r.
+ *   q, k, v, dout        [sp][B][Ns][H][d] bf16; lse the forward's final one
+ *   workspace            as filled by ulysses_ring_attn_bwd_prepare
+ *   dq_acc, dk_acc,      [sp][B][Ns][H][d] float running sums, indexed by the
+ *   dv_acc               chunk they belong to (set at step 0, added to later)
+ *   dq, dk, dv           [sp][B][Ns][H][d] bf16: a query chunk's dq is written
+ *                        at its rank's last step, a key/value chunk's dk, dv at
+ *                        its last visit (i == sp-1-j when causal, sp-1 otherwise)
+ * Steps run in order 0, 1, .., sp-1 after one prepare call.
+ * Errors: as ulysses_ring_attn_bwd_prepare.
+ */
+int ulysses_ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* dout,
+                               const float* lse, const void* workspace, size_t workspace_bytes,
+                               float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
+                               int step, int sp, int B, int Ns, int H, int d, int causal, int dtype,
+                               void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ulysses_status_string(int status);
 

@@ -30,6 +30,8 @@ def test_library_exports_every_declared_function():
     assert set(names) == {
         "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string",
+        "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
+        "ulysses_ring_attn_bwd_step",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -105,3 +107,33 @@ def test_binding_validates_cu_seqlens():
             uly.DocPacking(bad, 8, "cpu")
     p = uly.DocPacking([0, 3, 3, 8], 8, "cpu")
     assert (p.ndoc, p.max_doc_len) == (3, 5)
+
+
+def test_ring_argument_errors():
+    lib = uly.library()
+    f = lib.ulysses_ring_attn_fwd_step
+    ok = dict(step=0, sp=4, B=1, Ns=8, H=2, d=64, causal=1, dtype=1)
+
+    def call(**kw):
+        a = {**ok, **kw}
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, a["step"], a["sp"], a["B"], a["Ns"], a["H"], a["d"],
+                 a["causal"], a["dtype"], None)
+
+    assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL  # o_acc
+    assert call(step=-1) == EINVAL
+    assert call(step=4) == EINVAL  # steps are 0 .. sp-1
+    assert call(Ns=0) == EINVAL
+    assert call(dtype=0) == EUNSUP  # bf16 only
+    assert call(d=96) == EUNSUP
+
+    need = lib.ulysses_ring_attn_bwd_workspace_bytes(4, 1, 8, 2, 64, 1)
+    assert need == 2 * 4 * 1 * 2 * 8 * 4
+    assert lib.ulysses_ring_attn_bwd_workspace_bytes(4, 1, 8, 2, 64, 0) == 0
+    prep = lib.ulysses_ring_attn_bwd_prepare
+    assert prep(FAKE, FAKE, FAKE, FAKE, need - 1, 4, 1, 8, 2, 64, 1, None) == EWS
+    assert prep(FAKE, FAKE, None, FAKE, need, 4, 1, 8, 2, 64, 1, None) == EINVAL
+    step = lib.ulysses_ring_attn_bwd_step
+    ptrs = [FAKE] * 5
+    assert step(*ptrs, FAKE, need, *([FAKE] * 6), 4, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL  # step
+    assert step(*ptrs, None, need, *([FAKE] * 6), 0, 4, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert step(*ptrs, FAKE, need, *([FAKE] * 5), None, 0, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL

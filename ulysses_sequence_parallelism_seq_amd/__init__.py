@@ -13,6 +13,11 @@ Functions carry the C names:
   ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)
   ulysses_attn_bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)
   ulysses_attn_bwd_workspace_bytes(...), ulysses_status_string(code)
+  ulysses_ring_attn_fwd_step(q, k, v, step, ...) one ring step (running o_acc, lse)
+  ulysses_ring_attn_bwd_prepare(o, dout, lse)     D and lse*log2(e) into a workspace
+  ulysses_ring_attn_bwd_step(q, k, v, dout, lse, workspace, step, ...)
+  ulysses_ring_attn_bwd_workspace_bytes(...)
+and two loops over the ring steps, ring_attn_fwd and ring_attn_bwd.
 """
 
 from __future__ import annotations
@@ -54,9 +59,15 @@ def library() -> ctypes.CDLL:
         lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.ulysses_attn_bwd_workspace_bytes.restype = sz
         lib.ulysses_attn_bwd.argtypes = [vp] * 10 + [sz, vp] + [i] * 9 + [vp]
+        lib.ulysses_ring_attn_fwd_step.argtypes = [vp] * 6 + [i] * 8 + [vp]
+        lib.ulysses_ring_attn_bwd_workspace_bytes.argtypes = [i] * 6
+        lib.ulysses_ring_attn_bwd_workspace_bytes.restype = sz
+        lib.ulysses_ring_attn_bwd_prepare.argtypes = [vp] * 4 + [sz] + [i] * 6 + [vp]
+        lib.ulysses_ring_attn_bwd_step.argtypes = [vp] * 6 + [sz] + [vp] * 6 + [i] * 8 + [vp]
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
-        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd"):
+        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
+                     "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -210,6 +221,103 @@ def ulysses_attn_bwd(q, k, v, o, dout, lse, cu_seqlens=None, causal: bool = True
     return dq, dk, dv
 
 
+# ---------------------------------------------------------------- ring attention
+# q, k, v, dout, o: [sp, B, Ns, H, d] bf16 chunks (rank r holds tokens r*Ns ..);
+# lse: [sp, B, H, Ns] float32.
+
+
+def _ring_shape(q):
+    if q.dim() != 5:
+        raise ValueError("ring attention takes [sp, B, Ns, H, d] chunks")
+    if q.dtype != torch.bfloat16:
+        raise TypeError("ring attention runs in bfloat16")
+    return tuple(q.shape)
+
+
+def ulysses_ring_attn_fwd_step(q, k, v, step: int, causal: bool = True, o=None, o_acc=None, lse=None):
+    """One forward ring step; returns (o, o_acc, lse). Pass the previous step's o_acc and lse back in."""
+    sp, B, Ns, H, d = _ring_shape(q)
+    for t in (k, v):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v must share shape and dtype")
+    o = torch.empty_like(q) if o is None else o
+    o_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device) if o_acc is None else o_acc
+    lse = torch.empty((sp, B, H, Ns), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(o, q.shape, q.dtype, "o")
+    _expect(o_acc, q.shape, torch.float32, "o_acc")
+    _expect(lse, (sp, B, H, Ns), torch.float32, "lse")
+    _require_device(q, k, v, o, o_acc, lse)
+    _check("ulysses_ring_attn_fwd_step", library().ulysses_ring_attn_fwd_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_acc), _ptr(lse), int(step), sp, B, Ns, H, d,
+        int(bool(causal)), ULY_BF16, _stream(q)))
+    return o, o_acc, lse
+
+
+def ring_attn_fwd(q, k, v, causal: bool = True, o=None, o_acc=None, lse=None):
+    """All sp forward ring steps in order; returns (o, lse)."""
+    for step in range(q.shape[0]):
+        o, o_acc, lse = ulysses_ring_attn_fwd_step(q, k, v, step, causal, o, o_acc, lse)
+    return o, lse
+
+
+def ulysses_ring_attn_bwd_workspace_bytes(sp: int, B: int, Ns: int, H: int, d: int) -> int:
+    return int(library().ulysses_ring_attn_bwd_workspace_bytes(sp, B, Ns, H, d, ULY_BF16))
+
+
+def ulysses_ring_attn_bwd_prepare(o, dout, lse, workspace=None):
+    """D = rowsum(dO * O) and lse * log2(e) into the (returned) workspace."""
+    sp, B, Ns, H, d = _ring_shape(o)
+    if dout.shape != o.shape or dout.dtype != o.dtype:
+        raise ValueError("o and dout must share shape and dtype")
+    need = ulysses_ring_attn_bwd_workspace_bytes(sp, B, Ns, H, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device)
+    _expect(lse, (sp, B, H, Ns), torch.float32, "lse")
+    _require_device(o, dout, lse, workspace)
+    _check("ulysses_ring_attn_bwd_prepare", library().ulysses_ring_attn_bwd_prepare(
+        _ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        sp, B, Ns, H, d, ULY_BF16, _stream(o)))
+    return workspace
+
+
+def ulysses_ring_attn_bwd_step(q, k, v, dout, lse, workspace, step: int, causal: bool = True,
+                               dq_acc=None, dk_acc=None, dv_acc=None, dq=None, dk=None, dv=None):
+    """One backward ring step; returns (dq, dk, dv, dq_acc, dk_acc, dv_acc)."""
+    sp, B, Ns, H, d = _ring_shape(q)
+    for t in (k, v, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, dout must share shape and dtype")
+    f32 = lambda: torch.empty(q.shape, dtype=torch.float32, device=q.device)  # noqa: E731
+    dq_acc = f32() if dq_acc is None else dq_acc
+    dk_acc = f32() if dk_acc is None else dk_acc
+    dv_acc = f32() if dv_acc is None else dv_acc
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq_acc", dq_acc), ("dk_acc", dk_acc), ("dv_acc", dv_acc)):
+        _expect(t, q.shape, torch.float32, name)
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, q.shape, q.dtype, name)
+    _expect(lse, (sp, B, H, Ns), torch.float32, "lse")
+    _require_device(q, k, v, dout, lse, workspace, dq_acc, dk_acc, dv_acc, dq, dk, dv)
+    _check("ulysses_ring_attn_bwd_step", library().ulysses_ring_attn_bwd_step(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(dq_acc), _ptr(dk_acc), _ptr(dv_acc),
+        _ptr(dq), _ptr(dk), _ptr(dv), int(step), sp, B, Ns, H, d, int(bool(causal)), ULY_BF16, _stream(q)))
+    return dq, dk, dv, dq_acc, dk_acc, dv_acc
+
+
+def ring_attn_bwd(q, k, v, o, dout, lse, causal: bool = True, workspace=None):
+    """Prepare plus all sp backward ring steps in order; returns (dq, dk, dv)."""
+    workspace = ulysses_ring_attn_bwd_prepare(o, dout, lse, workspace)
+    bufs = (None,) * 6
+    for step in range(q.shape[0]):
+        dq, dk, dv, dqa, dka, dva = ulysses_ring_attn_bwd_step(q, k, v, dout, lse, workspace, step, causal,
+                                                               bufs[3], bufs[4], bufs[5], *bufs[:3])
+        bufs = (dq, dk, dv, dqa, dka, dva)
+    return bufs[0], bufs[1], bufs[2]
+
+
 __all__ = [
     "DocPacking",
     "UlyssesError",
@@ -220,4 +328,10 @@ __all__ = [
     "ulysses_attn_bwd",
     "ulysses_attn_bwd_workspace_bytes",
     "ulysses_status_string",
+    "ulysses_ring_attn_fwd_step",
+    "ulysses_ring_attn_bwd_prepare",
+    "ulysses_ring_attn_bwd_step",
+    "ulysses_ring_attn_bwd_workspace_bytes",
+    "ring_attn_fwd",
+    "ring_attn_bwd",
 ]

@@ -62,7 +62,36 @@ struct BwdArgs {
   int causal;
   float sl2;    // log2(e) / sqrt(d)
   float scale;  // 1 / sqrt(d)
+  // ring step only: fp32 running sums of dQ (per query chunk) and dK, dV (per
+  // key/value chunk), same layout as dq; the step; ring size and batch rows
+  float* dq_acc;
+  float* dk_acc;
+  float* dv_acc;
+  int step, sp, B;
 };
+
+// Ring step geometry of a row g = c * B + b whose chunk c is held by the
+// workgroup: chunk c meets chunk c - step (query side, kq) or c + step (key
+// side) mod sp. Returns false when the causal mask hides the whole block.
+struct RingBlock {
+  int other;   // the other chunk's row (its chunk * B + b)
+  int causal;  // 1: the causal diagonal block
+  bool first, last;
+};
+__device__ __forceinline__ bool ring_block(const BwdArgs& a, int g, bool query_side, RingBlock& rb) {
+  const int c = g / a.B, b = g - (g / a.B) * a.B;
+  int oc = query_side ? c - a.step : c + a.step;
+  if (oc < 0) oc += a.sp;
+  if (oc >= a.sp) oc -= a.sp;
+  const int qc = query_side ? c : oc, kc = query_side ? oc : c;  // query chunk, key chunk
+  if (a.causal && kc > qc) return false;
+  rb.other = oc * a.B + b;
+  rb.causal = a.causal && kc == qc;
+  rb.first = a.step == 0;
+  // a query chunk's last block is key chunk 0 (causal); a key chunk's is query chunk sp - 1
+  rb.last = !a.causal ? a.step == a.sp - 1 : (query_side ? a.step == c : a.step == a.sp - 1 - c);
+  return true;
+}
 
 __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int& e) {
   s = 0;
@@ -113,12 +142,31 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
   }
 }
 
+// Ring steps: elements i0 .. i0+3 of an accumulator times s, added to the four
+// fp32 running sums at acc (stored as they are at the first step); at the
+// last step the sums also go to out as bf16.
+__device__ __forceinline__ void add_store4(float* acc, const f32x16& v, int i0, float s, bool first, bf16* out) {
+  float4 x = make_float4(v[i0] * s, v[i0 + 1] * s, v[i0 + 2] * s, v[i0 + 3] * s);
+  if (!first) {
+    const float4 y = *reinterpret_cast<const float4*>(acc);
+    x.x += y.x;
+    x.y += y.y;
+    x.z += y.z;
+    x.w += y.w;
+  }
+  *reinterpret_cast<float4*>(acc) = x;
+  if (out) *reinterpret_cast<uint2*>(out) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
+}
+
 // --------------------------------------------------------------------- dq kernel
 constexpr int kDqBQ = 256;       // queries per workgroup (32 per wave)
 constexpr int kDqThreads = 512;  // 8 waves sharing each K/V tile, one workgroup per CU
 constexpr int kDqBK = 64;   // keys per tile
 
-template <int D>
+// kRing: one ring step; row g = r * B + b holds rank r's queries, its keys and
+// values come from chunk (r - step) mod sp, and dQ is added to dq_acc (written
+// to dq at the rank's last step).
+template <int D, bool kRing>
 __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) {
   using L = RowTile<D>;
   constexpr int KK = D / 16, CB = D / 32;
@@ -140,6 +188,14 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
   const size_t rs = (size_t)a.Hl * D;
   const uint32_t row_bytes = (uint32_t)rs * 2u;
   const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
+  size_t kvbase = base;
+  int causal = a.causal;
+  RingBlock rb{g, a.causal, true, true};
+  if constexpr (kRing) {
+    if (!ring_block(a, g, true, rb)) return;  // before any barrier
+    causal = rb.causal;
+    kvbase = ((size_t)rb.other * a.N * a.Hl + hd) * D;
+  }
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int qi = q0 + 32 * w + l32;
@@ -161,7 +217,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
   const float lse2 = qvalid ? a.lse[(size_t)unit * a.N + qi] * kLog2e : 0.f;
   const float dlt = qvalid ? a.delta[(size_t)unit * a.N + qi] : 0.f;
 
-  const int kend = a.causal ? min(e, q0 + kDqBQ) : e;
+  const int kend = causal ? min(e, q0 + kDqBQ) : e;
   const int ntiles = (kend - s + kDqBK - 1) / kDqBK;
 
   f32x16 dqacc[CB];
@@ -171,7 +227,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
     for (int i = 0; i < 16; ++i) dqacc[cb][i] = 0.f;
 
   auto rsrc_at = [&](const bf16* p, int kt0) {
-    return make_rsrc(p + base + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
+    return make_rsrc(p + kvbase + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
   };
   // K/V tiles by direct-to-LDS loads: tile t+1 goes out before the math of
   // tile t and is waited for before its barrier
@@ -189,8 +245,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
       dma.issue(rsrc_at(a.v, kt0 + kDqBK), vn);
     }
 
-    if (!a.causal || kt0 <= q0 + 32 * w + 31) {
-      const bool need_mask = (a.causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
+    if (!causal || kt0 <= q0 + 32 * w + 31) {
+      const bool need_mask = (causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
       // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (lane = query,
       // element i is key kt0 + blk*32 + 8*(i/4) + 4*half + (i%4)), dS^T, then
       // dQ^T += K^T dS^T with K^T read from the K tile by transposing reads
@@ -211,7 +267,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= e || (a.causal && key > qi)) sacc[i] = -INFINITY;
+            if (key >= e || (causal && key > qi)) sacc[i] = -INFINITY;
           }
         }
         uint4 dsb[2];
@@ -244,11 +300,22 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 
   if (qvalid) {
     bf16* out = a.dq + base + (size_t)qi * rs;
+    if constexpr (kRing) {
+      float* acc = a.dq_acc + base + (size_t)qi * rs;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
-        *reinterpret_cast<uint2*>(out + cb * 32 + 8 * gq + 4 * half) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
+        for (int gq = 0; gq < 4; ++gq) {
+          const int c = cb * 32 + 8 * gq + 4 * half;
+          add_store4(acc + c, dqacc[cb], 4 * gq, a.scale, rb.first, rb.last ? out + c : nullptr);
+        }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<uint2*>(out + cb * 32 + 8 * gq + 4 * half) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
+    }
   }
 }
 
@@ -320,7 +387,10 @@ struct KvDma {
   }
 };
 
-template <int D>
+// kRing: one ring step; row g = j * B + b holds key/value chunk j, its queries
+// (Q, dO, lse, D) come from rank (j + step) mod sp, and dK, dV are added to
+// dk_acc, dv_acc (written to dk, dv at the chunk's last step).
+template <int D, bool kRing>
 __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a) {
   using L = RowTile<D>;
   constexpr int KK = D / 16;
@@ -344,6 +414,16 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   const size_t rs = (size_t)a.Hl * D;
   const uint32_t row_bytes = (uint32_t)rs * 2u;
   const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
+  size_t qbase = base;
+  int qunit = unit;
+  int causal = a.causal;
+  RingBlock rb{g, a.causal, true, true};
+  if constexpr (kRing) {
+    if (!ring_block(a, g, false, rb)) return;  // before any barrier
+    causal = rb.causal;
+    qbase = ((size_t)rb.other * a.N * a.Hl + hd) * D;
+    qunit = rb.other * a.Hl + hd;
+  }
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const bool producer = w < 4;
@@ -351,7 +431,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   const int kp0 = kb0 + 32 * pair;  // the pair's first key
   const int kj = kp0 + l32;         // this lane's key
 
-  const int qstart = a.causal ? kb0 : s;
+  const int qstart = causal ? kb0 : s;
   const int ntiles = (e - qstart + kKvBQ - 1) / kKvBQ;
   // Query tiles are walked from the document end down: every workgroup of a
   // head then reads the same tile at about the same time, from the XCD's L2.
@@ -359,12 +439,12 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
 
   KvDma<D> dma;
   dma.init(w, lane, row_bytes);
-  const float* lse2_u = a.lse2 + (size_t)unit * a.N;
-  const float* dl_u = a.delta + (size_t)unit * a.N;
+  const float* lse2_u = a.lse2 + (size_t)qunit * a.N;
+  const float* dl_u = a.delta + (size_t)qunit * a.N;
   auto load_tile = [&](int i, KvStage<D>& st) {
     const int qt0 = qlast - i * kKvBQ;
     const long long span = (long long)(e - qt0) * row_bytes;
-    dma.issue(make_rsrc(a.q + base + (size_t)qt0 * rs, span), make_rsrc(a.dout + base + (size_t)qt0 * rs, span),
+    dma.issue(make_rsrc(a.q + qbase + (size_t)qt0 * rs, span), make_rsrc(a.dout + qbase + (size_t)qt0 * rs, span),
               make_rsrc(lse2_u + qt0, (long long)(e - qt0) * 4), make_rsrc(dl_u + qt0, (long long)(e - qt0) * 4),
               st, w, lane);
   };
@@ -414,7 +494,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
       if (i >= ntiles) return;
       const int qt0 = qlast - i * kKvBQ;
       // tiles that cross the diagonal or a document end are masked element by element
-      const bool need_mask = (a.causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
+      const bool need_mask = (causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         f32x16 sacc, pacc;
@@ -454,7 +534,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
 #pragma unroll
           for (int x = 0; x < 16; ++x) {
             const int qq = qt0 + 32 * qb + 8 * (x >> 2) + 4 * half + (x & 3);
-            if (qq >= e || kj >= e || (a.causal && kj > qq)) p[x] = 0.f;
+            if (qq >= e || kj >= e || (causal && kj > qq)) p[x] = 0.f;
           }
         }
 #pragma unroll
@@ -525,14 +605,27 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
     if (kj < e) {
       bf16* ko = a.dk + base + (size_t)kj * rs;
       bf16* vo = a.dv + base + (size_t)kj * rs;
+      if constexpr (kRing) {
+        float* ka = a.dk_acc + base + (size_t)kj * rs;
+        float* va = a.dv_acc + base + (size_t)kj * rs;
 #pragma unroll
-      for (int c = 0; c < CB; ++c)
+        for (int c = 0; c < CB; ++c)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int col = 32 * c + 8 * gq + 4 * half;
-          *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[c], 4 * gq, a.scale);
-          *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[c], 4 * gq, 1.f);
-        }
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = 32 * c + 8 * gq + 4 * half;
+            add_store4(ka + col, dkacc[c], 4 * gq, a.scale, rb.first, rb.last ? ko + col : nullptr);
+            add_store4(va + col, dvacc[c], 4 * gq, 1.f, rb.first, rb.last ? vo + col : nullptr);
+          }
+      } else {
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int col = 32 * c + 8 * gq + 4 * half;
+            *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[c], 4 * gq, a.scale);
+            *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[c], 4 * gq, 1.f);
+          }
+      }
     }
   }
 }
@@ -564,6 +657,10 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   a.causal = g.causal;
   a.scale = 1.0f / sqrtf((float)g.d);
   a.sl2 = uly::kLog2e * a.scale;
+  a.dq_acc = a.dk_acc = a.dv_acc = nullptr;
+  a.step = 0;
+  a.sp = 1;
+  a.B = 1;
   const int maxlen = g.cu ? g.max_doc_len : g.N;
   hipStream_t st = (hipStream_t)stream;
 
@@ -586,13 +683,80 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   if (g.d == 64) {
     hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
                        lse, delta, a.lse2, g.N, g.Hl, rows);
-    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<64>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL(attn_dq_bf16_kernel<64>, dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<64, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   } else {
     hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
                        lse, delta, a.lse2, g.N, g.Hl, rows);
-    hipLaunchKernelGGL(attn_dkdv_bf16_kernel<128>, dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL(attn_dq_bf16_kernel<128>, dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<128, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+  }
+  return launch_status();
+}
+
+int launch_ring_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
+                                 const AttnGeom& g, void* stream) {
+  const long long rows = (long long)g.G * g.Hl * g.N;
+  const int rpb = kThreads / (g.d / 8);
+  const long long dblocks = (rows + rpb - 1) / rpb;
+  if (dblocks > 0x7fffffffLL) return ULY_ESHAPE;
+  const bf16* ob = static_cast<const bf16*>(o);
+  const bf16* db = static_cast<const bf16*>(dout);
+  float* lse2 = delta + (size_t)rows;
+  hipStream_t st = (hipStream_t)stream;
+  if (g.d == 64)
+    hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, ob, db, lse, delta,
+                       lse2, g.N, g.Hl, rows);
+  else
+    hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, ob, db, lse, delta,
+                       lse2, g.N, g.Hl, rows);
+  return launch_status();
+}
+
+int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                         const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
+                         void* dv, const AttnGeom& g, int sp, int B, int step, void* stream) {
+  BwdArgs a;
+  a.q = static_cast<const bf16*>(q);
+  a.k = static_cast<const bf16*>(k);
+  a.v = static_cast<const bf16*>(v);
+  a.o = nullptr;
+  a.dout = static_cast<const bf16*>(dout);
+  a.lse = lse;
+  a.delta = const_cast<float*>(delta);
+  a.lse2 = const_cast<float*>(delta) + (size_t)g.G * g.Hl * g.N;
+  a.dq = static_cast<bf16*>(dq);
+  a.dk = static_cast<bf16*>(dk);
+  a.dv = static_cast<bf16*>(dv);
+  a.cu = nullptr;
+  a.ndoc = 1;
+  a.units = g.G * g.Hl;
+  a.Hl = g.Hl;
+  a.N = g.N;
+  a.causal = g.causal;
+  a.scale = 1.0f / sqrtf((float)g.d);
+  a.sl2 = uly::kLog2e * a.scale;
+  a.dq_acc = dq_acc;
+  a.dk_acc = dk_acc;
+  a.dv_acc = dv_acc;
+  a.step = step;
+  a.sp = sp;
+  a.B = B;
+  BwdArgs aq = a;
+  aq.nslots = (g.N + kDqBQ - 1) / kDqBQ;
+  BwdArgs akv = a;
+  akv.nslots = (g.N + kKvBK - 1) / kKvBK;
+  const long long qblocks = (long long)aq.nslots * a.units;
+  const long long kvblocks = (long long)akv.nslots * a.units;
+  const long long ug = a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup;
+  if ((long long)aq.nslots * ug > 0x7fffffffLL || (long long)akv.nslots * ug > 0x7fffffffLL) return ULY_ESHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (g.d == 64) {
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, true>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<64, true>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+  } else {
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, true>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<128, true>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   }
   return launch_status();
 }

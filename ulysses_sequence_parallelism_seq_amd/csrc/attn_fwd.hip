@@ -74,6 +74,10 @@ struct FwdArgs {
   int N;
   int causal;
   float sl2;  // log2(e) / sqrt(d)
+  // ring step only: running normalised O (fp32, same layout as o), the step,
+  // and the ring size and batch rows that make up the G = sp * B stacked rows
+  float* o_acc;
+  int step, sp, B;
 };
 
 // Lazy rescale: the running max used in the exponentials only moves when a
@@ -83,7 +87,12 @@ struct FwdArgs {
 // normalisation uses the same m, so the result is unchanged.
 constexpr float kRescaleSlack = 8.0f;
 
-template <int D>
+// kRing: one step of ring attention. Row g = r * B + b holds rank r's query
+// chunk; its keys and values come from chunk j = (r - step) mod sp, the whole
+// chunk (j < r, or not causal), its causal diagonal (j == r) or none (j > r).
+// The kernel starts from the running state (o_acc, lse) of the previous steps
+// and leaves the merged state there; o is written at the rank's last step.
+template <int D, bool kRing>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   using S = FwdSmem<D>;
   constexpr int KK = D / 16;  // MFMA k-steps over the head dimension
@@ -109,9 +118,21 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
   const size_t rs = (size_t)a.Hl * D;
   const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
+  size_t kvbase = base;
+  int causal = a.causal;
+  bool first = true, last = true;
+  if constexpr (kRing) {
+    const int r = g / a.B, b = g - (g / a.B) * a.B;
+    const int j = r >= a.step ? r - a.step : r - a.step + a.sp;
+    if (a.causal && j > r) return;  // no key of this chunk is visible; before any barrier
+    causal = a.causal && j == r;
+    kvbase = ((size_t)(j * a.B + b) * a.N * a.Hl + hd) * D;
+    first = a.step == 0;
+    last = a.causal ? a.step == r : a.step == a.sp - 1;
+  }
   const bf16* qb = a.q + base;
-  const bf16* kb = a.k + base;
-  const bf16* vb = a.v + base;
+  const bf16* kb = a.k + kvbase;
+  const bf16* vb = a.v + kvbase;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
@@ -128,7 +149,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int kk = 0; kk < KK; ++kk) qreg[kk] = buf_load16(qr, qoff + 32u * kk);
   }
 
-  const int kend = a.causal ? min(e, q0 + kBQ) : e;
+  const int kend = causal ? min(e, q0 + kBQ) : e;
   const int ntiles = (kend - s + kBK - 1) / kBK;
 
   f32x16 oacc[CB];
@@ -137,6 +158,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) oacc[cb][i] = 0.f;
   float m_run = -1e30f, l_run = 0.f;
+  if constexpr (kRing) {
+    // continue the online softmax from the previous steps: with the running
+    // max at lse (log2 units) the earlier keys weigh exactly 1 in total and
+    // the normalised O_acc is their weighted sum
+    if (!first && qvalid) {
+      const float* arow = a.o_acc + base + (size_t)qi * rs;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 x = *reinterpret_cast<const float4*>(arow + cb * 32 + 8 * gq + 4 * half);
+          oacc[cb][4 * gq] = x.x;
+          oacc[cb][4 * gq + 1] = x.y;
+          oacc[cb][4 * gq + 2] = x.z;
+          oacc[cb][4 * gq + 3] = x.w;
+        }
+      m_run = a.lse[(size_t)unit * a.N + qi] * kLog2e;
+      l_run = half == 0 ? 1.f : 0.f;  // the two half-waves' partial sums add up to 1
+    }
+  }
 
   TileDma<D, kBK, kThreads / 64> dma;
   dma.init(w, lane, row_bytes);
@@ -155,7 +196,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       dma.issue(rsrc_at(vb, kt0 + kBK), vn);
     }
 
-    const bool wave_active = !a.causal || kt0 <= q0 + 32 * w + 31;
+    const bool wave_active = !causal || kt0 <= q0 + 32 * w + 31;
     if (wave_active) {
       // S^T for the tile's 32-key blocks
       constexpr int NB = kBK / 32;
@@ -171,7 +212,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         }
       }
       // mask where the tile crosses the diagonal or the document end (scale applied in the exponent)
-      const bool need_mask = (a.causal && kt0 + kBK - 1 > q0) || kt0 + kBK > e;
+      const bool need_mask = (causal && kt0 + kBK - 1 > q0) || kt0 + kBK > e;
       float mloc = -INFINITY;
       if (need_mask) {
 #pragma unroll
@@ -180,7 +221,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
           for (int i = 0; i < 16; ++i) {
             float x = sacc[blk][i];
             const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= e || (a.causal && key > qi)) x = -INFINITY;
+            if (key >= e || (causal && key > qi)) x = -INFINITY;
             sacc[blk][i] = x;
             mloc = fmaxf(mloc, x);
           }
@@ -204,21 +245,25 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
           for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
       }
 
-      // P^T = exp2(x - m), packed to bf16 as the B operand of four 16-key MFMA steps
+      // P^T = exp2(x - m), packed to bf16 as the B operand of four 16-key MFMA
+      // steps. The row sum takes the tile's 32 values pairwise before adding
+      // them to the running sum: over a long row that adds far fewer roundings
+      // than one value at a time (which matters when many terms are alike).
+      static_assert(NB == 2, "the pairwise tile sum covers four groups of eight");
       uint4 pb[2 * NB];
+      float ls[2 * NB];
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
           float p[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = fast_exp2(fmaf(sacc[blk][8 * mm + j], a.sl2, -m_run));
-            l_run += p[j];
-          }
+          for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(sacc[blk][8 * mm + j], a.sl2, -m_run));
+          ls[blk * 2 + mm] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
           pb[blk * 2 + mm] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
         }
+      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
       // O^T += V^T P^T: the A operand is V^T read from the row-major V tile
       // with transposing reads; step (blk, mm) covers keys blk*32 + 16*mm ..
@@ -242,14 +287,26 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const float l_tot = l_run + swap_halves(l_run);
   if (qvalid) {
     const float inv = 1.f / l_tot;
-    bf16* orow = a.o + base + (size_t)qi * rs;
+    if constexpr (kRing) {
+      float* arow = a.o_acc + base + (size_t)qi * rs;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int c = cb * 32 + 8 * gq + 4 * half;
-        *reinterpret_cast<uint2*>(orow + c) = pack4_scaled(oacc[cb], 4 * gq, inv);
-      }
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<float4*>(arow + cb * 32 + 8 * gq + 4 * half) =
+              make_float4(oacc[cb][4 * gq] * inv, oacc[cb][4 * gq + 1] * inv, oacc[cb][4 * gq + 2] * inv,
+                          oacc[cb][4 * gq + 3] * inv);
+    }
+    if (last) {
+      bf16* orow = a.o + base + (size_t)qi * rs;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int c = cb * 32 + 8 * gq + 4 * half;
+          *reinterpret_cast<uint2*>(orow + c) = pack4_scaled(oacc[cb], 4 * gq, inv);
+        }
+    }
     if (half == 0) a.lse[(size_t)unit * a.N + qi] = (m_run + log2f(l_tot)) * kLn2;
   }
 }
@@ -275,15 +332,50 @@ int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, f
   a.N = g.N;
   a.causal = g.causal;
   a.sl2 = uly::kLog2e / sqrtf((float)g.d);
+  a.o_acc = nullptr;
+  a.step = 0;
+  a.sp = 1;
+  a.B = 1;
   const long long blocks = (long long)a.nq_slots * a.ndoc * a.units;
   // the tile decode also forms nq_slots * ndoc * kUnitGroup in int
   const long long span = (long long)a.nq_slots * a.ndoc * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
   if (span > 0x7fffffffLL) return ULY_ESHAPE;
   hipStream_t st = (hipStream_t)stream;
   if (g.d == 64)
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<64>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL(attn_fwd_bf16_kernel<128>, dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, false>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  return launch_status();
+}
+
+int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* o_acc, float* lse,
+                         const AttnGeom& g, int sp, int B, int step, void* stream) {
+  FwdArgs a;
+  a.q = static_cast<const bf16*>(q);
+  a.k = static_cast<const bf16*>(k);
+  a.v = static_cast<const bf16*>(v);
+  a.o = static_cast<bf16*>(o);
+  a.lse = lse;
+  a.cu = nullptr;
+  a.ndoc = 1;
+  a.nq_slots = (g.N + kBQ - 1) / kBQ;
+  a.units = g.G * g.Hl;
+  a.Hl = g.Hl;
+  a.N = g.N;
+  a.causal = g.causal;
+  a.sl2 = uly::kLog2e / sqrtf((float)g.d);
+  a.o_acc = o_acc;
+  a.step = step;
+  a.sp = sp;
+  a.B = B;
+  const long long blocks = (long long)a.nq_slots * a.units;
+  const long long span = (long long)a.nq_slots * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
+  if (span > 0x7fffffffLL) return ULY_ESHAPE;
+  hipStream_t st = (hipStream_t)stream;
+  if (g.d == 64)
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
   return launch_status();
 }
 

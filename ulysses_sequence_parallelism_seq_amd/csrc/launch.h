@@ -28,4 +28,13 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* delta, const AttnGeom& a, void* stream);
 
+// Ring attention steps (bf16): rows g = chunk * B + b of Ns tokens, H heads.
+int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* o_acc, float* lse,
+                         const AttnGeom& a, int sp, int B, int step, void* stream);
+int launch_ring_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
+                                 const AttnGeom& a, void* stream);
+int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                         const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
+                         void* dv, const AttnGeom& a, int sp, int B, int step, void* stream);
+
 }  // namespace uly_host

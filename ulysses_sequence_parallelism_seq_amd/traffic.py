@@ -23,7 +23,7 @@ import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = ["csrc/attn_bwd.hip", "csrc/common.h", "csrc/permute.hip"]
-BWD_KERNELS = ("attn_dkdv_bf16_kernel<128>", "attn_dq_bf16_kernel<128>", "delta_bf16_kernel<128>")
+BWD_KERNELS = ("attn_dkdv_bf16_kernel<128, false>", "attn_dq_bf16_kernel<128, false>", "delta_bf16_kernel<128>")
 COPY_KERNEL = "permute_runs<true>"
 
 
