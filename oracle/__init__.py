@@ -14,6 +14,8 @@ Contents:
   ring       the ring-attention variant: blockwise attention of each rank's
              query chunk against key/value chunks passed around a ring,
              partial results merged by their log-sum-exp; its backward.
+  loss       the sequence-parallel loss aggregation: per-rank mean loss and
+             counted-token count, combined as a count-weighted mean.
 
 Every function here is pinned by tests that do not call it twice: closed
 forms, finite differences, brute-force loops, an independent library
@@ -29,4 +31,5 @@ from .attention import (  # noqa: F401
     attn_bwd_dkdv_cols,
     doc_ids,
 )
+from .loss import sp_loss, rank_losses, aggregate  # noqa: F401
 from .ring import ring_fwd, ring_bwd, ring_chunk, block_mode, block_attn, merge, stitch, stitch_lse  # noqa: F401
