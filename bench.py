@@ -24,6 +24,11 @@ change; sp forward ring steps (each rank's queries against the key/value
 chunk passed to it, partial results merged by log-sum-exp), the D pre-pass,
 then sp backward ring steps. Same FLOP count, same value definition.
 
+With --variant loss it times the sequence-parallel loss aggregation on the
+workload's tokens instead (sp ranks x B rows x N/sp tokens: per-token fp32
+losses and int64 labels, 30% of them -100): value = bytes read (12 per
+token) per second, against the HBM peak.
+
 Prints one JSON line. --gpus above 1 exits: this build measures one GPU.
 """
 
@@ -218,7 +223,7 @@ def main():
     ap.add_argument("--workload", default="long", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--variant", default="ulysses", choices=["ulysses", "ring"])
+    ap.add_argument("--variant", default="ulysses", choices=["ulysses", "ring", "loss"])
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -231,6 +236,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cu = workloads.workload_cu_seqlens(w)
+    if args.variant == "loss":
+        return loss_main(args, w, dev)
     if args.variant == "ring":
         if cu is not None or w.dtype != "bf16":
             print("the ring variant runs bf16 workloads with one document per row", file=sys.stderr)
@@ -324,6 +331,73 @@ def main():
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def loss_main(args, w, dev):
+    shape = (w.sp, w.B, w.Ns)
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    token_loss = torch.rand(shape, generator=g, device=dev) * 8.0
+    labels = torch.randint(0, 32000, shape, generator=g, device=dev, dtype=torch.int64)
+    labels[torch.rand(shape, generator=g, device=dev) < 0.3] = -100
+    out = uly.ulysses_sp_loss(token_loss, labels)
+    ws = torch.empty(max(int(uly.library().ulysses_sp_loss_workspace_bytes(*shape)), 8), dtype=torch.uint8,
+                     device=dev)
+    calls = 200 * max(1, args.steps)
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(20 * max(1, args.warmup)):
+        uly.ulysses_sp_loss(token_loss, labels, workspace=ws, loss=out[0], rank_loss=out[1], good_tokens=out[2])
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(calls):
+        uly.ulysses_sp_loss(token_loss, labels, workspace=ws, loss=out[0], rank_loss=out[1], good_tokens=out[2])
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / calls
+    nbytes = 12 * w.sp * w.B * w.Ns
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": "SP loss aggregation GB/s (bytes read per second)",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": calls,
+        "warmup": 20 * max(1, args.warmup),
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+int64 in, f64 sums",
+        "data": "synthetic (seeded per-token losses, 30% of labels -100)",
+        "config": {
+            "workload": f"{w.name}'s tokens: sp={w.sp} ranks x B={w.B} x {w.Ns} tokens",
+            "tokens": w.sp * w.B * w.Ns,
+            "launches_per_call": 2,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "ulysses_sp_loss (partial + final kernels of one call)",
+            "achieved": round(gbs, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "bytes_per_launch": nbytes,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        tl, lab = token_loss.cpu().numpy(), labels.cpu().numpy()
+        reps, t0 = 0, time.perf_counter()
+        while time.perf_counter() - t0 < min(args.cpu_seconds, 5.0):
+            oracle.sp_loss(tl, lab)
+            reps += 1
+        t = (time.perf_counter() - t0) / reps
+        result["cpu_baseline"] = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1,
+                                  "kind": "oracle", "sample": f"the float64 oracle on the same tokens, {reps} calls"}
     print(json.dumps(result), flush=True)
 
 

@@ -15,6 +15,11 @@
  *   - congresoia365 article, section "El Desafío del Entrenamiento de
  *     Secuencias Largas": memory-efficient attention keeps O(N) state and
  *     never stores the N x N score matrix.
+ *   - ColossalAI docs, "Sequence Parallelism": ring attention, the other
+ *     sequence-parallel mode (the ulysses_ring_attn_* calls).
+ *   - jianying88 guide to DeepSpeed Ulysses in Transformers, section on the
+ *     work Trainer does by itself: the count-weighted loss across SP ranks
+ *     (ulysses_sp_loss).
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is device memory owned by the caller, contiguous
@@ -27,9 +32,9 @@
  *   - Arguments are checked on the host before anything is enqueued; a call
  *     that returns an error has enqueued nothing. The contents of device
  *     buffers (e.g. cu_seqlens) are never read on the host.
- *   - dtype is ULY_F32 (float) or ULY_BF16 (bfloat16, round-to-nearest-even
- *     outputs). Accumulation is always in fp32.
- *   - Head width d must be 64 or 128.
+ *   - For the permute and attention calls, dtype is ULY_F32 (float) or
+ *     ULY_BF16 (bfloat16, round-to-nearest-even outputs); accumulation is
+ *     always in fp32 or wider. Head width d must be 64 or 128.
  */
 #ifndef ULYSSES_H
 #define ULYSSES_H
@@ -196,6 +201,30 @@ int ulysses_ring_attn_bwd_step(const void* q, const void* k, const void* v, cons
                                float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
                                int step, int sp, int B, int Ns, int H, int d, int causal, int dtype,
                                void* stream);
+
+/*
+ * Sequence-parallel loss aggregation (jianying88 guide to DeepSpeed Ulysses
+ * in Transformers, section on the work Trainer does by itself, item 3), for
+ * sp virtual ranks held on one device. Rank r's loss is the mean of its
+ * per-token losses over its counted tokens (label != ignore_index), good_r
+ * their number; the batch loss is
+ *   loss = sum_r loss_r * good_r / sum_r good_r   over ranks with good_r > 0,
+ * the mean over every counted token of the batch. A rank without counted
+ * tokens gets loss_r = 0 and drops out; with none anywhere loss = 0. Tokens
+ * that do not count contribute nothing, whatever their loss value holds.
+ *   token_loss   [sp][B][Ns] float, each rank's per-token losses
+ *   labels       [sp][B][Ns] int64, the shifted labels (ignore_index = not counted)
+ *   rank_loss    [sp] float out;  good_tokens [sp] int64 out;  loss [1] float out
+ *   workspace    >= ulysses_sp_loss_workspace_bytes(sp, B, Ns) bytes, 8-byte
+ *                aligned; contents on entry ignored
+ * Sums are fp64 in a fixed order (bit-reproducible). sp <= 4096.
+ * Errors: ULY_EINVAL (null pointer, size <= 0), ULY_ESHAPE (sp > 4096),
+ * ULY_EWORKSPACE, ULY_EHIP.
+ */
+size_t ulysses_sp_loss_workspace_bytes(int sp, int B, int Ns);
+int ulysses_sp_loss(const float* token_loss, const long long* labels, float* rank_loss,
+                    long long* good_tokens, float* loss, void* workspace, size_t workspace_bytes,
+                    int sp, int B, int Ns, int ignore_index, void* stream);
 
 /* Static English text for a status code (never NULL). */
 const char* ulysses_status_string(int status);

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_function():
         "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string",
         "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
-        "ulysses_ring_attn_bwd_step",
+        "ulysses_ring_attn_bwd_step", "ulysses_sp_loss_workspace_bytes", "ulysses_sp_loss",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -137,3 +137,17 @@ def test_ring_argument_errors():
     assert step(*ptrs, FAKE, need, *([FAKE] * 6), 4, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL  # step
     assert step(*ptrs, None, need, *([FAKE] * 6), 0, 4, 1, 8, 2, 64, 1, 1, None) == EWS
     assert step(*ptrs, FAKE, need, *([FAKE] * 5), None, 0, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL
+
+
+def test_sp_loss_argument_errors():
+    lib = uly.library()
+    need = lib.ulysses_sp_loss_workspace_bytes(8, 1, 16384)
+    assert need == 8 * 4 * 16  # 4 partials of 4096 tokens per rank, fp64 sum + int64 count each
+    assert lib.ulysses_sp_loss_workspace_bytes(0, 1, 8) == 0
+    assert lib.ulysses_sp_loss_workspace_bytes(4097, 1, 8) == 0
+    f = lib.ulysses_sp_loss
+    assert f(None, FAKE, FAKE, FAKE, FAKE, FAKE, need, 8, 1, 16384, -100, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 8, 0, 16384, -100, None) == EINVAL
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 5000, 1, 8, -100, None) == ESHAPE
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 8, 1, 16384, -100, None) == EWS
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, need, 8, 1, 16384, -100, None) == EWS

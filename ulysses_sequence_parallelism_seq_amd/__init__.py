@@ -18,6 +18,7 @@ Functions carry the C names:
   ulysses_ring_attn_bwd_step(q, k, v, dout, lse, workspace, step, ...)
   ulysses_ring_attn_bwd_workspace_bytes(...)
 and two loops over the ring steps, ring_attn_fwd and ring_attn_bwd.
+  ulysses_sp_loss(token_loss, labels)      -> (loss, rank_loss, good_tokens)
 """
 
 from __future__ import annotations
@@ -64,10 +65,14 @@ def library() -> ctypes.CDLL:
         lib.ulysses_ring_attn_bwd_workspace_bytes.restype = sz
         lib.ulysses_ring_attn_bwd_prepare.argtypes = [vp] * 4 + [sz] + [i] * 6 + [vp]
         lib.ulysses_ring_attn_bwd_step.argtypes = [vp] * 6 + [sz] + [vp] * 6 + [i] * 8 + [vp]
+        lib.ulysses_sp_loss_workspace_bytes.argtypes = [i, i, i]
+        lib.ulysses_sp_loss_workspace_bytes.restype = sz
+        lib.ulysses_sp_loss.argtypes = [vp] * 6 + [sz] + [i] * 4 + [vp]
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
         for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
-                     "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step"):
+                     "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
+                     "ulysses_sp_loss"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -318,6 +323,37 @@ def ring_attn_bwd(q, k, v, o, dout, lse, causal: bool = True, workspace=None):
     return bufs[0], bufs[1], bufs[2]
 
 
+# ------------------------------------------------------- SP loss aggregation
+
+
+def ulysses_sp_loss(token_loss, labels, ignore_index: int = -100, workspace=None, loss=None, rank_loss=None,
+                    good_tokens=None):
+    """Count-weighted loss of sp ranks; returns (loss [1] f32, rank_loss [sp] f32, good_tokens [sp] int64).
+
+    token_loss: [sp, B, Ns] float32 per-token losses; labels: [sp, B, Ns] int64.
+    """
+    if token_loss.dim() != 3 or token_loss.dtype != torch.float32:
+        raise ValueError("token_loss must be [sp, B, Ns] float32")
+    if labels.shape != token_loss.shape or labels.dtype != torch.int64:
+        raise ValueError("labels must be int64 with token_loss's shape")
+    sp, B, Ns = token_loss.shape
+    dev = token_loss.device
+    need = int(library().ulysses_sp_loss_workspace_bytes(sp, B, Ns))
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    rank_loss = torch.empty(sp, dtype=torch.float32, device=dev) if rank_loss is None else rank_loss
+    good_tokens = torch.empty(sp, dtype=torch.int64, device=dev) if good_tokens is None else good_tokens
+    _expect(loss, (1,), torch.float32, "loss")
+    _expect(rank_loss, (sp,), torch.float32, "rank_loss")
+    _expect(good_tokens, (sp,), torch.int64, "good_tokens")
+    _require_device(token_loss, labels, workspace, loss, rank_loss, good_tokens)
+    _check("ulysses_sp_loss", library().ulysses_sp_loss(
+        _ptr(token_loss), _ptr(labels), _ptr(rank_loss), _ptr(good_tokens), _ptr(loss), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), sp, B, Ns, int(ignore_index), _stream(token_loss)))
+    return loss, rank_loss, good_tokens
+
+
 __all__ = [
     "DocPacking",
     "UlyssesError",
@@ -334,4 +370,5 @@ __all__ = [
     "ulysses_ring_attn_bwd_workspace_bytes",
     "ring_attn_fwd",
     "ring_attn_bwd",
+    "ulysses_sp_loss",
 ]
