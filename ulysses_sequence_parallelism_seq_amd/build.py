@@ -33,6 +33,11 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# Per-source extra flags. The forward kernel runs about 2% faster with the
+# scheduler's max-ilp strategy (measured per kernel with rocprofv3 on the long
+# workload); the backward kernels are about 1% slower with it, so only the
+# forward's source takes it.
+FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _run(cmd, verbose):
@@ -48,7 +53,8 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     flags = FLAGS + list(extra_flags or [])
     objs = [os.path.join(BUILD, os.path.splitext(s)[0] + ".o") for s in SOURCES]
-    cmds = [[HIPCC, *flags, "-c", os.path.join(CSRC, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    cmds = [[HIPCC, *flags, *FILE_FLAGS.get(s, []), "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
     with cf.ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))
     tmp = LIB + ".tmp"

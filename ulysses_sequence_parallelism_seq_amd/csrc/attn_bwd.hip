@@ -24,9 +24,10 @@
 //     document end down to its first key (causal). Producer waves compute
 //     S = Q K^T, dP = dO V^T (lane = key; K and V resident as B operands),
 //     P and dS; consumer waves, one tile behind, accumulate dV^T += dO^T P
-//     and dK^T += Q^T dS with the A operands read transposed from the
-//     row-major Q and dO tiles; the accumulators hold one key per lane, so
-//     the final stores are 4 consecutive columns per lane.
+//     and dK^T += Q^T dS (64 keys x half the columns each) with the A
+//     operands read transposed from the row-major Q and dO tiles; the
+//     accumulators hold one key per lane, so the final stores are 4
+//     consecutive columns per lane.
 // The MFMA k index of a 16-wide step maps to tokens the same way as in the
 // forward kernel, so P and dS feed the MFMA straight from the accumulators.
 
@@ -327,9 +328,11 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 //     per tile it computes S = Q K^T and dP = dO V^T for both 32-query blocks
 //     (lane = key), then P = exp2(S * log2(e) / sqrt(d) - lse2) and
 //     dS = P (dP - D), packed to bf16 in the order the MFMA k index takes them;
-//   * consumer p + 4: one tile behind, dV^T += dO^T P and dK^T += Q^T dS for
-//     all D columns of the 32 keys, with the A operands read transposed from
-//     the row-major Q and dO tiles and P, dS taken from the producer through LDS.
+//   * consumers, one tile behind: consumer c accumulates dV^T += dO^T P and
+//     dK^T += Q^T dS for the 64 keys of producers 2 (c/2) and 2 (c/2) + 1 and
+//     half of the D columns, with the A operands read transposed from the
+//     row-major Q and dO tiles (each serving both key blocks) and P, dS taken
+//     from the producers through LDS (each serving both column blocks).
 // The producer's exponentials run while the consumer keeps the SIMD's matrix
 // core busy. Query tiles (Q, dO, lse2, D) arrive by direct-to-LDS loads one
 // tile ahead, in three stages: the producer reads tile i while the consumer
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   const bool producer = w < 4;
   const int pair = w & 3;
   const int kp0 = kb0 + 32 * pair;  // the pair's first key
-  const int kj = kp0 + l32;         // this lane's key
+  const int kj = kp0 + l32;         // this lane's key (producer waves)
 
   const int qstart = causal ? kb0 : s;
   const int ntiles = (e - qstart + kKvBQ - 1) / kKvBQ;
@@ -558,73 +561,86 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
     };
     tile_loop(produce, publish);
   } else {
-    // dK^T and dV^T of the pair's 32 keys, all D columns (lane = key)
-    f32x16 dkacc[CB], dvacc[CB];
+    // Consumer c takes the P/dS of producer pairs 2 (c/2) and 2 (c/2) + 1 (64
+    // keys) and accumulates dK^T, dV^T for half of the D columns, those of
+    // column blocks CH (c % 2) .. CH (c % 2) + CH - 1: every A fragment (dO^T,
+    // Q^T) it reads serves both key blocks and every P/dS operand both column
+    // blocks.
+    constexpr int CH = CB / 2;
+    const int kp_first = 2 * (pair >> 1);  // first producer pair of this consumer
+    const int cb0 = CH * (pair & 1);
+    f32x16 dkacc[2][CH], dvacc[2][CH];  // [key block][column block]
 #pragma unroll
-    for (int c = 0; c < CB; ++c)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) dkacc[c][i] = dvacc[c][i] = 0.f;
-    // the previous tile: dV^T += dO^T P and dK^T += Q^T dS over both query
-    // blocks. Step (qb, c) needs four A fragments (dO^T and Q^T, two 16-query
-    // halves); the fragments of the next step are read while this step's
-    // MFMAs run.
+      for (int c = 0; c < CH; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dkacc[kb][c][i] = dvacc[kb][c][i] = 0.f;
+    // the previous tile, in four steps (query block qb, 16-query half hf):
+    // A = dO^T, Q^T of those 16 queries for the CH column blocks, B = P, dS
+    // of the two key blocks; the next step's operands are read while this
+    // step's MFMAs run
     auto consume = [&](int i, const KvStage<D>&, const KvStage<D>& st) {
       if (i < 1) return;
-      constexpr int NSTEP = 2 * CB;
-      auto rd = [&](int step, bf16x8* f) {
-        const int qb = step / CB, c = step % CB;
-        f[0] = a_from_rows<D>(st.dout, 32 * qb, 32 * c, lane);
-        f[1] = a_from_rows<D>(st.dout, 32 * qb + 16, 32 * c, lane);
-        f[2] = a_from_rows<D>(st.q, 32 * qb, 32 * c, lane);
-        f[3] = a_from_rows<D>(st.q, 32 * qb + 16, 32 * c, lane);
-      };
-      bf16x8 fr[2][4];
-      uint4 opnd[2][4];
+      auto rd = [&](int step, bf16x8 (*fa)[2], uint4 (*fb)[2]) {
+        const int qb = step >> 1, hf = step & 1;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) opnd[0][j] = xbuf[((pair * 2 + 0) * 4 + j) * 64 + lane];
-      rd(0, fr[0]);
-#pragma unroll
-      for (int step = 0; step < NSTEP; ++step) {
-        const int qb = step / CB, c = step % CB;
-        if (step + 1 < NSTEP) rd(step + 1, fr[(step + 1) & 1]);
-        if (step == CB - 1) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) opnd[1][j] = xbuf[((pair * 2 + 1) * 4 + j) * 64 + lane];
+        for (int c = 0; c < CH; ++c) {
+          fa[c][0] = a_from_rows<D>(st.dout, 32 * qb + 16 * hf, 32 * (cb0 + c), lane);
+          fa[c][1] = a_from_rows<D>(st.q, 32 * qb + 16 * hf, 32 * (cb0 + c), lane);
         }
-        const bf16x8* f = fr[step & 1];
-        dvacc[c] = mfma32(f[0], as_bf16x8(opnd[qb][0]), dvacc[c]);
-        dkacc[c] = mfma32(f[2], as_bf16x8(opnd[qb][2]), dkacc[c]);
-        dvacc[c] = mfma32(f[1], as_bf16x8(opnd[qb][1]), dvacc[c]);
-        dkacc[c] = mfma32(f[3], as_bf16x8(opnd[qb][3]), dkacc[c]);
-        // the reads of step + 1 stay ahead of these MFMAs, later ones stay behind
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          fb[kb][0] = xbuf[(((kp_first + kb) * 2 + qb) * 4 + hf) * 64 + lane];
+          fb[kb][1] = xbuf[(((kp_first + kb) * 2 + qb) * 4 + 2 + hf) * 64 + lane];
+        }
+      };
+      bf16x8 fa[2][CH][2];
+      uint4 fb[2][2][2];
+      rd(0, fa[0], fb[0]);
+#pragma unroll
+      for (int step = 0; step < 4; ++step) {
+        if (step + 1 < 4) rd(step + 1, fa[(step + 1) & 1], fb[(step + 1) & 1]);
+        const int cur = step & 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            dvacc[kb][c] = mfma32(fa[cur][c][0], as_bf16x8(fb[cur][kb][0]), dvacc[kb][c]);
+            dkacc[kb][c] = mfma32(fa[cur][c][1], as_bf16x8(fb[cur][kb][1]), dkacc[kb][c]);
+          }
         __builtin_amdgcn_sched_barrier(0);
       }
     };
     tile_loop(consume, [](int) {});
 
-    if (kj < e) {
-      bf16* ko = a.dk + base + (size_t)kj * rs;
-      bf16* vo = a.dv + base + (size_t)kj * rs;
-      if constexpr (kRing) {
-        float* ka = a.dk_acc + base + (size_t)kj * rs;
-        float* va = a.dv_acc + base + (size_t)kj * rs;
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
+    for (int kb = 0; kb < 2; ++kb) {
+      const int kc = kb0 + 32 * (kp_first + kb) + l32;  // this lane's key in key block kb
+      if (kc < e) {
+        bf16* ko = a.dk + base + (size_t)kc * rs;
+        bf16* vo = a.dv + base + (size_t)kc * rs;
+        if constexpr (kRing) {
+          float* ka = a.dk_acc + base + (size_t)kc * rs;
+          float* va = a.dv_acc + base + (size_t)kc * rs;
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = 32 * c + 8 * gq + 4 * half;
-            add_store4(ka + col, dkacc[c], 4 * gq, a.scale, rb.first, rb.last ? ko + col : nullptr);
-            add_store4(va + col, dvacc[c], 4 * gq, 1.f, rb.first, rb.last ? vo + col : nullptr);
-          }
-      } else {
+          for (int c = 0; c < CH; ++c)
 #pragma unroll
-        for (int c = 0; c < CB; ++c)
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = 32 * (cb0 + c) + 8 * gq + 4 * half;
+              add_store4(ka + col, dkacc[kb][c], 4 * gq, a.scale, rb.first, rb.last ? ko + col : nullptr);
+              add_store4(va + col, dvacc[kb][c], 4 * gq, 1.f, rb.first, rb.last ? vo + col : nullptr);
+            }
+        } else {
 #pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const int col = 32 * c + 8 * gq + 4 * half;
-            *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[c], 4 * gq, a.scale);
-            *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[c], 4 * gq, 1.f);
-          }
+          for (int c = 0; c < CH; ++c)
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int col = 32 * (cb0 + c) + 8 * gq + 4 * half;
+              *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[kb][c], 4 * gq, a.scale);
+              *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[kb][c], 4 * gq, 1.f);
+            }
+        }
       }
     }
   }
