@@ -151,3 +151,13 @@ def test_sp_loss_argument_errors():
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 5000, 1, 8, -100, None) == ESHAPE
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 8, 1, 16384, -100, None) == EWS
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, need, 8, 1, 16384, -100, None) == EWS
+
+
+def test_ring_binding_needs_running_state_after_step_0():
+    import torch
+
+    q = torch.zeros(2, 1, 8, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        uly.ulysses_ring_attn_fwd_step(q, q, q, 1, True)
+    with pytest.raises(ValueError):
+        uly.ulysses_ring_attn_bwd_step(q, q, q, q, torch.zeros(2, 1, 2, 8), torch.zeros(8, dtype=torch.uint8), 1)

@@ -245,6 +245,8 @@ def ulysses_ring_attn_fwd_step(q, k, v, step: int, causal: bool = True, o=None, 
     for t in (k, v):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k, v must share shape and dtype")
+    if step > 0 and (o is None or o_acc is None or lse is None):
+        raise ValueError("steps after the first continue from the previous step's o, o_acc and lse")
     o = torch.empty_like(q) if o is None else o
     o_acc = torch.empty(q.shape, dtype=torch.float32, device=q.device) if o_acc is None else o_acc
     lse = torch.empty((sp, B, H, Ns), dtype=torch.float32, device=q.device) if lse is None else lse
@@ -292,6 +294,8 @@ def ulysses_ring_attn_bwd_step(q, k, v, dout, lse, workspace, step: int, causal:
     for t in (k, v, dout):
         if t.shape != q.shape or t.dtype != q.dtype:
             raise ValueError("q, k, v, dout must share shape and dtype")
+    if step > 0 and any(t is None for t in (dq_acc, dk_acc, dv_acc, dq, dk, dv)):
+        raise ValueError("steps after the first continue from the previous step's sums and outputs")
     f32 = lambda: torch.empty(q.shape, dtype=torch.float32, device=q.device)  # noqa: E731
     dq_acc = f32() if dq_acc is None else dq_acc
     dk_acc = f32() if dk_acc is None else dk_acc
