@@ -202,14 +202,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       constexpr int NB = kBK / 32;
       f32x16 sacc[NB];
 #pragma unroll
-      for (int blk = 0; blk < NB; ++blk) {
+      for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[blk][i] = 0.f;
+      // K fragment m (key block m / KK, k-step m % KK) is read PF MFMAs
+      // ahead of its use; the scheduling barriers keep that distance
+      constexpr int PF = 2;
+      auto kfrag = [&](int m) {
+        return *reinterpret_cast<const uint4*>(ks + S::L::off((m / KK) * 32 + l32, 16 * (m % KK) + 8 * half));
+      };
+      uint4 kf[PF + 1];
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const uint4 av = *reinterpret_cast<const uint4*>(ks + S::L::off(blk * 32 + l32, 16 * kk + 8 * half));
-          sacc[blk] = mfma32(as_bf16x8(av), as_bf16x8(qreg[kk]), sacc[blk]);
-        }
+      for (int m = 0; m < PF; ++m) kf[m] = kfrag(m);
+#pragma unroll
+      for (int m = 0; m < NB * KK; ++m) {
+        if (m + PF < NB * KK) kf[(m + PF) % (PF + 1)] = kfrag(m + PF);
+        sacc[m / KK] = mfma32(as_bf16x8(kf[m % (PF + 1)]), as_bf16x8(qreg[m % KK]), sacc[m / KK]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // mask where the tile crosses the diagonal or the document end (scale applied in the exponent)
       const bool need_mask = (causal && kt0 + kBK - 1 > q0) || kt0 + kBK > e;
@@ -233,9 +242,12 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
             mloc = fmaxf(mloc, sacc[blk][i]);
           }
       }
-      mloc = fmaxf(mloc, swap_halves(mloc)) * a.sl2;
-      if (__any(mloc > m_run + kRescaleSlack)) {
-        const float m_new = fmaxf(m_run, mloc);
+      // The two half-waves hold different keys of the same queries. Whether
+      // the running max must move is decided on each half's own maximum (the
+      // row max clears the slack iff one of the halves does); the row max
+      // itself, which needs an exchange between the halves, only when it moves.
+      if (__any(mloc * a.sl2 > m_run + kRescaleSlack)) {
+        const float m_new = fmaxf(m_run, fmaxf(mloc, swap_halves(mloc)) * a.sl2);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
