@@ -64,9 +64,10 @@ extern "C" {
  *   x_head [sp][B][N][H/sp][d]   shard r holds all N tokens of heads [r*H/sp, (r+1)*H/sp)
  *   x_head[r][b][s*N/sp + t][h][:] = x_seq[s][b][t][r*H/sp + h][:]
  * N is the full sequence length. Elements are copied as raw bits (bit-exact,
- * NaN payloads and -0 kept). x_seq and x_head must not overlap.
- * Errors: ULY_EINVAL (null, size <= 0), ULY_ESHAPE (N % sp, H % sp),
- * ULY_EUNSUPPORTED (dtype, d), ULY_EHIP.
+ * NaN payloads and -0 kept). x_seq and x_head must not overlap and must be
+ * 16-byte aligned.
+ * Errors: ULY_EINVAL (null, size <= 0, overlap, misaligned), ULY_ESHAPE
+ * (N % sp, H % sp), ULY_EUNSUPPORTED (dtype, d), ULY_EHIP.
  */
 int ulysses_seq_to_head(const void* x_seq, void* x_head, int B, int N, int H, int d, int sp,
                         int dtype, void* stream);

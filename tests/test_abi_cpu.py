@@ -56,6 +56,9 @@ def test_permute_argument_errors():
     assert f(FAKE, ctypes.c_void_p(0x1000 + 64), 1, 8, 4, 64, 2, 1, None) == EINVAL
     g = lib.ulysses_head_to_seq
     assert g(FAKE, ctypes.c_void_p(0x100000), 1, 6, 4, 64, 4, 1, None) == ESHAPE
+    # 16-byte accesses: misaligned buffers are rejected
+    assert f(ctypes.c_void_p(0x1002), ctypes.c_void_p(0x100000), 1, 8, 4, 64, 2, 1, None) == EINVAL
+    assert g(FAKE, ctypes.c_void_p(0x100008), 1, 8, 4, 64, 2, 1, None) == EINVAL
 
 
 def test_attention_argument_errors():

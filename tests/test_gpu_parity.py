@@ -26,6 +26,8 @@ pytestmark = pytest.mark.gpu
     (3, 2, 7, 6, 64, "bf16"),
     (1, 1, 5, 2, 128, "fp32"),
     (8, 1, 33, 16, 128, "bf16"),
+    (2, 1, 10, 6, 64, "bf16"),      # 3 heads per rank: 24-chunk runs (not a power of two)
+    (3, 1, 9, 9, 64, "fp32"),       # 3 ranks, 3 heads each: neither sp nor the run a power of two
 ])
 def test_permute_bit_exact(sp, B, Ns, H, d, dtype):
     say("permute", sp, B, Ns, H, d, dtype)

@@ -5,11 +5,19 @@
 // Both layouts are made of "runs": the Hl*d elements of one (rank, batch row,
 // token) in the head-sharded layout are the same Hl*d contiguous elements of
 // one (shard, batch row, token, head block) in the sequence-sharded layout.
-// A run is 256 B to 1 KiB at the shapes of interest, so both the reads and
-// the writes are whole contiguous segments. Every thread moves U 16-byte
-// chunks: all U loads are issued before the first store (memory-level
-// parallelism), and consecutive threads touch consecutive chunks (coalescing).
-// The kernel is a pure copy of bits and therefore exact for any content.
+// A run is R 16-byte chunks (256 B to 1 KiB at the shapes of interest).
+//
+// The grid carries the coordinates, so a chunk's two addresses cost a few
+// integer operations, and consecutive threads write consecutive chunks of
+// the output (contiguous writes matter more than contiguous reads here):
+//   * seq -> head: blockIdx.z = shard s, blockIdx.y = (rank r, batch row b),
+//     x = (token t within the shard, chunk w within the run);
+//   * head -> seq: blockIdx.z = shard s, blockIdx.y = batch row b,
+//     x = (token t, rank r, chunk w);
+// with shifts where R and sp are powers of two, divisions otherwise. The
+// reads are contiguous within each run. Every thread moves kUnroll chunks,
+// all loads before the first store; loads and stores are non-temporal (the
+// data streams through once). A pure copy of bits, exact for any content.
 
 #include "common.h"
 
@@ -17,63 +25,88 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
+constexpr uint32_t kChunksPerBlock = kThreads * kUnroll;
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// 16-byte non-temporal load and store
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ void st_nt(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
 
 struct PermuteGeom {
-  uint32_t R;   // 16-byte chunks per run
-  uint32_t N;   // full sequence length
-  uint32_t Ns;  // N / sp
+  uint32_t R;        // 16-byte chunks per run
+  int32_t rshift;    // log2(R) when R is a power of two, else -1
+  int32_t spshift;   // log2(sp) when sp is a power of two, else -1
+  uint32_t Ns;       // tokens per shard (N / sp)
   uint32_t B;
   uint32_t sp;
-  uint64_t run_bytes;
-  uint64_t total_chunks;
+  uint32_t rb_count; // sp * B
+  uint64_t run16;    // R (as 64-bit)
 };
 
-// Byte offset of the source run feeding output run q.
-template <bool kSeqToHead>
-__device__ __forceinline__ uint64_t source_run(uint32_t q, const PermuteGeom& g) {
-  if (kSeqToHead) {
-    // output x_head[r][b][n], n = s*Ns + t  <-  input x_seq[s][b][t][r-th head block]
-    uint32_t n = q % g.N;
-    uint32_t rb = q / g.N;
-    uint32_t b = rb % g.B;
-    uint32_t r = rb / g.B;
-    uint32_t s = n / g.Ns;
-    uint32_t t = n - s * g.Ns;
-    uint64_t token = ((uint64_t)s * g.B + b) * g.Ns + t;  // row of x_seq
-    return (token * g.sp + r) * g.run_bytes;
-  } else {
-    // output x_seq[s][b][t][r-th head block]  <-  input x_head[r][b][s*Ns + t]
-    uint32_t r = q % g.sp;
-    uint32_t rest = q / g.sp;
-    uint32_t t = rest % g.Ns;
-    rest /= g.Ns;
-    uint32_t b = rest % g.B;
-    uint32_t s = rest / g.B;
-    uint64_t token = ((uint64_t)r * g.B + b) * g.N + (uint64_t)s * g.Ns + t;  // row of x_head
-    return token * g.run_bytes;
+// seq -> head: blockIdx.y = (rank r, batch row b), x over (t, w) of the
+// head-sharded output, which is contiguous in that order.
+__global__ __launch_bounds__(kThreads) void permute_seq_to_head(const uint4* __restrict__ src,
+                                                                uint4* __restrict__ dst, PermuteGeom g) {
+  const uint32_t s = blockIdx.z;
+  const uint32_t slab = g.Ns * g.R;
+  for (uint32_t rb = blockIdx.y; rb < g.rb_count; rb += gridDim.y) {
+    const uint32_t r = rb / g.B, b = rb - (rb / g.B) * g.B;
+    // output run (r*B + b)*N + s*Ns + t; input run ((s*B + b)*Ns + t)*sp + r
+    const uint64_t out0 = ((uint64_t)rb * g.sp + s) * g.Ns * g.run16;
+    const uint64_t in0 = (((uint64_t)s * g.B + b) * g.Ns * g.sp + r) * g.run16;
+    const uint64_t in_tstride = (uint64_t)g.sp * g.run16;
+    uint4 buf[kUnroll];
+    const uint32_t c0 = blockIdx.x * kChunksPerBlock + threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint32_t c = c0 + j * kThreads;
+      if (c < slab) {
+        const uint32_t t = g.rshift >= 0 ? c >> g.rshift : c / g.R;
+        const uint32_t w = c - t * g.R;
+        buf[j] = ld_nt(src + in0 + (uint64_t)t * in_tstride + w);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint32_t c = c0 + j * kThreads;
+      if (c < slab) st_nt(dst + out0 + c, buf[j]);
+    }
   }
 }
 
-template <bool kSeqToHead>
-__global__ __launch_bounds__(kThreads) void permute_runs(const uint8_t* __restrict__ src,
-                                                         uint8_t* __restrict__ dst, PermuteGeom g) {
-  const uint64_t base = (uint64_t)blockIdx.x * (kThreads * kUnroll) + threadIdx.x;
-  uint4 buf[kUnroll];
-  uint64_t dst_off[kUnroll];
+// head -> seq: blockIdx.y = batch row b, x over (t, r, w) of the
+// sequence-sharded output, which is contiguous in that order.
+__global__ __launch_bounds__(kThreads) void permute_head_to_seq(const uint4* __restrict__ src,
+                                                                uint4* __restrict__ dst, PermuteGeom g) {
+  const uint32_t s = blockIdx.z;
+  const uint32_t slab = g.Ns * g.sp * g.R;
+  for (uint32_t b = blockIdx.y; b < g.B; b += gridDim.y) {
+    // output run ((s*B + b)*Ns + t)*sp + r; input run (r*B + b)*N + s*Ns + t
+    const uint64_t out0 = ((uint64_t)s * g.B + b) * g.Ns * g.sp * g.run16;
+    const uint64_t in0 = ((uint64_t)b * g.sp * g.Ns + (uint64_t)s * g.Ns) * g.run16;
+    const uint64_t in_rstride = (uint64_t)g.B * g.sp * g.Ns * g.run16;  // one rank further
+    uint4 buf[kUnroll];
+    const uint32_t c0 = blockIdx.x * kChunksPerBlock + threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    const uint64_t c = base + (uint64_t)j * kThreads;
-    dst_off[j] = c * 16;
-    if (c < g.total_chunks) {
-      const uint32_t q = (uint32_t)(c / g.R);
-      const uint32_t w = (uint32_t)(c - (uint64_t)q * g.R);
-      buf[j] = *reinterpret_cast<const uint4*>(src + source_run<kSeqToHead>(q, g) + (uint64_t)w * 16);
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint32_t c = c0 + j * kThreads;
+      if (c < slab) {
+        const uint32_t tr = g.rshift >= 0 ? c >> g.rshift : c / g.R;
+        const uint32_t w = c - tr * g.R;
+        const uint32_t t = g.spshift >= 0 ? tr >> g.spshift : tr / g.sp;
+        const uint32_t r = tr - t * g.sp;
+        buf[j] = ld_nt(src + in0 + (uint64_t)r * in_rstride + (uint64_t)t * g.run16 + w);
+      }
     }
-  }
 #pragma unroll
-  for (int j = 0; j < kUnroll; ++j) {
-    const uint64_t c = base + (uint64_t)j * kThreads;
-    if (c < g.total_chunks) *reinterpret_cast<uint4*>(dst + dst_off[j]) = buf[j];
+    for (int j = 0; j < kUnroll; ++j) {
+      const uint32_t c = c0 + j * kThreads;
+      if (c < slab) st_nt(dst + out0 + c, buf[j]);
+    }
   }
 }
 
@@ -87,25 +120,38 @@ int launch_permute(const void* src, void* dst, int B, int N, int H, int d, int s
   const uint64_t esz = uly_host::elem_size(dtype);
   const uint64_t Hl = (uint64_t)(H / sp);
   const uint64_t total_bytes = (uint64_t)B * N * H * d * esz;
-  // Run indices are 32-bit: sp * B * N runs.
-  if ((uint64_t)sp * B * N >= (1ULL << 32)) return ULY_ESHAPE;
   const uint8_t* s8 = static_cast<const uint8_t*>(src);
   uint8_t* d8 = static_cast<uint8_t*>(dst);
   if (s8 < d8 + total_bytes && d8 < s8 + total_bytes) return ULY_EINVAL;  // overlap
+  // 16-byte accesses need 16-byte aligned buffers (runs are multiples of 16 bytes)
+  if (((uintptr_t)src | (uintptr_t)dst) & 15) return ULY_EINVAL;
 
   PermuteGeom g;
-  g.run_bytes = Hl * d * esz;
-  g.R = (uint32_t)(g.run_bytes / 16);
-  g.N = (uint32_t)N;
+  const uint64_t run_bytes = Hl * d * esz;
+  g.R = (uint32_t)(run_bytes / 16);
+  g.rshift = g.spshift = -1;
+  for (int k = 0; k < 32; ++k) {
+    if ((1u << k) == g.R) g.rshift = k;
+    if ((1u << k) == (uint32_t)sp) g.spshift = k;
+  }
   g.Ns = (uint32_t)(N / sp);
   g.B = (uint32_t)B;
   g.sp = (uint32_t)sp;
-  g.total_chunks = total_bytes / 16;
-  const uint64_t per_block = (uint64_t)kThreads * kUnroll;
-  const uint64_t blocks = (g.total_chunks + per_block - 1) / per_block;
-  if (blocks > 0x7fffffffULL) return ULY_ESHAPE;
-  hipLaunchKernelGGL(permute_runs<kSeqToHead>, dim3((unsigned)blocks), dim3(kThreads), 0,
-                     (hipStream_t)stream, s8, d8, g);
+  g.run16 = g.R;
+  // a slab of output chunks is indexed in 32 bits; sp is the grid's z
+  const uint64_t slab = kSeqToHead ? (uint64_t)g.Ns * g.R : (uint64_t)g.Ns * g.sp * g.R;
+  if (slab + kChunksPerBlock >= (1ULL << 32) || sp > 65535 || (uint64_t)sp * B >= (1ULL << 32)) return ULY_ESHAPE;
+  g.rb_count = (uint32_t)(sp * B);
+  const uint64_t bx = (slab + kChunksPerBlock - 1) / kChunksPerBlock;
+  if (bx > 0x7fffffffULL) return ULY_ESHAPE;
+  const uint32_t ny = kSeqToHead ? g.rb_count : g.B;
+  const dim3 grid((unsigned)bx, ny < 65535u ? ny : 65535u, (unsigned)sp);
+  const uint4* s16 = reinterpret_cast<const uint4*>(s8);
+  uint4* d16 = reinterpret_cast<uint4*>(d8);
+  if (kSeqToHead)
+    hipLaunchKernelGGL(permute_seq_to_head, grid, dim3(kThreads), 0, (hipStream_t)stream, s16, d16, g);
+  else
+    hipLaunchKernelGGL(permute_head_to_seq, grid, dim3(kThreads), 0, (hipStream_t)stream, s16, d16, g);
   return uly_host::launch_status();
 }
 
@@ -124,7 +170,7 @@ extern "C" int ulysses_head_to_seq(const void* x_head, void* x_seq, int B, int N
 extern "C" const char* ulysses_status_string(int status) {
   switch (status) {
     case ULY_OK: return "ok";
-    case ULY_EINVAL: return "invalid argument (null pointer, size <= 0, or overlapping buffers)";
+    case ULY_EINVAL: return "invalid argument (null pointer, size <= 0, overlapping or misaligned buffers, or step out of range)";
     case ULY_ESHAPE: return "inconsistent shape (N % sp, H % sp, max_doc_len > N, or size limits)";
     case ULY_EUNSUPPORTED: return "unsupported dtype or head dimension (d must be 64 or 128)";
     case ULY_EWORKSPACE: return "workspace missing or too small";

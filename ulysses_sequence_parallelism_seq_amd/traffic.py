@@ -24,7 +24,7 @@ import sys
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCES = ["csrc/attn_bwd.hip", "csrc/common.h", "csrc/permute.hip"]
 BWD_KERNELS = ("attn_dkdv_bf16_kernel<128,false>", "attn_dq_bf16_kernel<128,false>", "delta_bf16_kernel<128>")
-COPY_KERNEL = "permute_runs<true>"
+COPY_KERNEL = "permute_seq_to_head"
 
 
 def sources_sha256() -> str:
@@ -37,7 +37,10 @@ def sources_sha256() -> str:
 
 def _short(name: str) -> str:
     """Kernel name without namespace, arguments or spaces (one token of the summary's lines)."""
-    return name.replace("void (anonymous namespace)::", "").replace("void ", "").split("(")[0].replace(" ", "")
+    for prefix in ("void ", "(anonymous namespace)::"):
+        if name.startswith(prefix):
+            name = name[len(prefix):]
+    return name.split("(")[0].replace(" ", "")
 
 
 def _per_dispatch(csv_dir: str, counter: str) -> dict:
