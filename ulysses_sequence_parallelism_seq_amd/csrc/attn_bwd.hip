@@ -106,40 +106,61 @@ __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int
 // ------------------------------------------------------------------ D pre-pass
 // D[unit][t] = sum_c dO[t][c] * O[t][c]; D/8 lanes per row, 16 bytes per lane.
 // Also lse2[unit][t] = lse[unit][t] * log2(e), the form the dK/dV kernel stages.
+// blockIdx.y = unit (g * Hl + h), blockIdx.x = a span of kDeltaPasses * 256 / (D/8)
+// tokens; each group of D/8 lanes takes kDeltaPasses rows, all loads (non-temporal:
+// O and dO stream through once) issued before the first product.
+constexpr int kDeltaPasses = 4;
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt16(const bf16* p) {
+  return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __restrict__ o,
                                                               const bf16* __restrict__ dout,
                                                               const float* __restrict__ lse,
                                                               float* __restrict__ delta,
                                                               float* __restrict__ lse2, int N, int Hl,
-                                                              long long rows) {
-  constexpr int LPR = D / 8;  // lanes per row
-  constexpr int RPB = kThreads / LPR;
+                                                              long long units) {
+  constexpr int LPR = D / 8;              // lanes per row
+  constexpr int RPP = kThreads / LPR;     // rows per pass
   const int sub = threadIdx.x % LPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
-  float acc = 0.f;
-  if (row < rows) {
-    // row enumerates (unit, t) with t fastest; unit = g * Hl + h
-    const long long unit = row / N;
-    const int t = (int)(row - unit * N);
+  const int t0 = blockIdx.x * (RPP * kDeltaPasses) + threadIdx.x / LPR;
+  for (long long unit = blockIdx.y; unit < units; unit += gridDim.y) {
     const long long g = unit / Hl;
     const int h = (int)(unit - g * Hl);
-    const size_t off = ((size_t)(g * N + t) * Hl + h) * D + sub * 8;
-    const uint4 ov = *reinterpret_cast<const uint4*>(o + off);
-    const uint4 dv = *reinterpret_cast<const uint4*>(dout + off);
-    const uint32_t* ow = reinterpret_cast<const uint32_t*>(&ov);
-    const uint32_t* dw = reinterpret_cast<const uint32_t*>(&dv);
+    const size_t tstride = (size_t)Hl * D;  // elements between tokens
+    const size_t base = ((size_t)g * N * Hl + h) * D + sub * 8;
+    uint4 ov[kDeltaPasses], dv[kDeltaPasses];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      acc = fmaf(bf16_bits_to_float(ow[j] & 0xffffu), bf16_bits_to_float(dw[j] & 0xffffu), acc);
-      acc = fmaf(bf16_bits_to_float(ow[j] >> 16), bf16_bits_to_float(dw[j] >> 16), acc);
+    for (int p = 0; p < kDeltaPasses; ++p) {
+      const int t = t0 + p * RPP;
+      if (t < N) {
+        ov[p] = ld_nt16(o + base + (size_t)t * tstride);
+        dv[p] = ld_nt16(dout + base + (size_t)t * tstride);
+      }
     }
-  }
 #pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
-  if (row < rows && sub == 0) {
-    delta[row] = acc;
-    lse2[row] = lse[row] * kLog2e;
+    for (int p = 0; p < kDeltaPasses; ++p) {
+      const int t = t0 + p * RPP;
+      float acc = 0.f;
+      if (t < N) {
+        const uint32_t* ow = reinterpret_cast<const uint32_t*>(&ov[p]);
+        const uint32_t* dw = reinterpret_cast<const uint32_t*>(&dv[p]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc = fmaf(bf16_bits_to_float(ow[j] & 0xffffu), bf16_bits_to_float(dw[j] & 0xffffu), acc);
+          acc = fmaf(bf16_bits_to_float(ow[j] >> 16), bf16_bits_to_float(dw[j] >> 16), acc);
+        }
+      }
+#pragma unroll
+      for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
+      if (t < N && sub == 0) {
+        const size_t row = (size_t)unit * N + t;
+        delta[row] = acc;
+        lse2[row] = lse[row] * kLog2e;
+      }
+    }
   }
 }
 
@@ -680,10 +701,8 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   const int maxlen = g.cu ? g.max_doc_len : g.N;
   hipStream_t st = (hipStream_t)stream;
 
-  const long long rows = (long long)a.units * g.N;
-  const int rpb = kThreads / (g.d / 8);
-  const long long dblocks = (rows + rpb - 1) / rpb;
-  if (dblocks > 0x7fffffffLL) return ULY_ESHAPE;
+  const int tpb = kDeltaPasses * kThreads / (g.d / 8);  // tokens per block
+  const dim3 dgrid((unsigned)((g.N + tpb - 1) / tpb), (unsigned)(a.units < 65535 ? a.units : 65535));
 
   BwdArgs aq = a;
   aq.nslots = (maxlen + kDqBQ - 1) / kDqBQ;
@@ -697,13 +716,13 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   if (span_q > 0x7fffffffLL || span_kv > 0x7fffffffLL) return ULY_ESHAPE;
 
   if (g.d == 64) {
-    hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
-                       lse, delta, a.lse2, g.N, g.Hl, rows);
+    hipLaunchKernelGGL(delta_bf16_kernel<64>, dgrid, dim3(kThreads), 0, st, a.o, a.dout,
+                       lse, delta, a.lse2, g.N, g.Hl, (long long)a.units);
     hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL((attn_dq_bf16_kernel<64, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   } else {
-    hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, a.o, a.dout,
-                       lse, delta, a.lse2, g.N, g.Hl, rows);
+    hipLaunchKernelGGL(delta_bf16_kernel<128>, dgrid, dim3(kThreads), 0, st, a.o, a.dout,
+                       lse, delta, a.lse2, g.N, g.Hl, (long long)a.units);
     hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL((attn_dq_bf16_kernel<128, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   }
@@ -713,19 +732,19 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
 int launch_ring_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
                                  const AttnGeom& g, void* stream) {
   const long long rows = (long long)g.G * g.Hl * g.N;
-  const int rpb = kThreads / (g.d / 8);
-  const long long dblocks = (rows + rpb - 1) / rpb;
-  if (dblocks > 0x7fffffffLL) return ULY_ESHAPE;
+  const long long units = (long long)g.G * g.Hl;
+  const int tpb = kDeltaPasses * kThreads / (g.d / 8);  // tokens per block
+  const dim3 dgrid((unsigned)((g.N + tpb - 1) / tpb), (unsigned)(units < 65535 ? units : 65535));
   const bf16* ob = static_cast<const bf16*>(o);
   const bf16* db = static_cast<const bf16*>(dout);
   float* lse2 = delta + (size_t)rows;
   hipStream_t st = (hipStream_t)stream;
   if (g.d == 64)
-    hipLaunchKernelGGL(delta_bf16_kernel<64>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, ob, db, lse, delta,
-                       lse2, g.N, g.Hl, rows);
+    hipLaunchKernelGGL(delta_bf16_kernel<64>, dgrid, dim3(kThreads), 0, st, ob, db, lse, delta,
+                       lse2, g.N, g.Hl, units);
   else
-    hipLaunchKernelGGL(delta_bf16_kernel<128>, dim3((unsigned)dblocks), dim3(kThreads), 0, st, ob, db, lse, delta,
-                       lse2, g.N, g.Hl, rows);
+    hipLaunchKernelGGL(delta_bf16_kernel<128>, dgrid, dim3(kThreads), 0, st, ob, db, lse, delta,
+                       lse2, g.N, g.Hl, units);
   return launch_status();
 }
 
