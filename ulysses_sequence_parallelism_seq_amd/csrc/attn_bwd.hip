@@ -222,6 +222,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int qi = q0 + 32 * w + l32;
   const bool qvalid = qi < e;
+  FragOffsets<D> fo;
+  fo.init(lane);
 
   // Q^T and dO^T as resident B operands (rows past the document end read as zero)
   uint4 qreg[KK], doreg[KK];
@@ -277,14 +279,28 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
         f32x16 sacc, pacc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+        // K and V fragments read two k-steps ahead of their MFMAs
+        auto rd = [&](int kk, uint4* f) {
+          const uint32_t off = fo.row_frag(blk, kk);
+          f[0] = lds_ld16(ks, off);
+          f[1] = lds_ld16(vs, off);
+        };
+        uint4 fr[3][2];
+        rd(0, fr[0]);
+        rd(1, fr[1]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          const int off = L::off(blk * 32 + l32, 16 * kk + 8 * half);
-          const uint4 ka = *reinterpret_cast<const uint4*>(ks + off);
-          const uint4 va = *reinterpret_cast<const uint4*>(vs + off);
-          sacc = mfma32(as_bf16x8(ka), as_bf16x8(qreg[kk]), sacc);
-          pacc = mfma32(as_bf16x8(va), as_bf16x8(doreg[kk]), pacc);
+          if (kk + 2 < KK) rd(kk + 2, fr[(kk + 2) % 3]);
+          sacc = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(qreg[kk]), sacc);
+          pacc = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(doreg[kk]), pacc);
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // K^T operands of the dQ MFMAs go out now and land during the exponentials
+        bf16x8 kt[CB][2];
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) kt[cb][mm] = a_from_rows_at<D>(ks, fo, 2 * blk + mm, cb);
         if (need_mask) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -308,7 +324,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int mm = 0; mm < 2; ++mm)
-            dqacc[cb] = mfma32(a_from_rows<D>(ks, 32 * blk + 16 * mm, 32 * cb, lane), as_bf16x8(dsb[mm]), dqacc[cb]);
+            dqacc[cb] = mfma32(kt[cb][mm], as_bf16x8(dsb[mm]), dqacc[cb]);
       }
     }
 
@@ -454,6 +470,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   const int pair = w & 3;
   const int kp0 = kb0 + 32 * pair;  // the pair's first key
   const int kj = kp0 + l32;         // this lane's key (producer waves)
+  FragOffsets<D> fo;
+  fo.init(lane);
 
   const int qstart = causal ? kb0 : s;
   const int ntiles = (e - qstart + kKvBQ - 1) / kKvBQ;
@@ -526,9 +544,9 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
         for (int x = 0; x < 16; ++x) sacc[x] = pacc[x] = 0.f;
         // Q and dO fragments read two k-steps ahead of their MFMAs
         auto rd = [&](int kk, uint4* f) {
-          const int off = L::off(32 * qb + l32, 16 * kk + 8 * half);
-          f[0] = *reinterpret_cast<const uint4*>(st.q + off);
-          f[1] = *reinterpret_cast<const uint4*>(st.dout + off);
+          const uint32_t off = fo.row_frag(qb, kk);
+          f[0] = lds_ld16(st.q, off);
+          f[1] = lds_ld16(st.dout, off);
         };
         uint4 fr[3][2];
         rd(0, fr[0]);
@@ -607,8 +625,8 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
         const int qb = step >> 1, hf = step & 1;
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
-          fa[c][0] = a_from_rows<D>(st.dout, 32 * qb + 16 * hf, 32 * (cb0 + c), lane);
-          fa[c][1] = a_from_rows<D>(st.q, 32 * qb + 16 * hf, 32 * (cb0 + c), lane);
+          fa[c][0] = a_from_rows_at<D>(st.dout, fo, 2 * qb + hf, cb0 + c);
+          fa[c][1] = a_from_rows_at<D>(st.q, fo, 2 * qb + hf, cb0 + c);
         }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {

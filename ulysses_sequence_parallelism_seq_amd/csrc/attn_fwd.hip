@@ -137,6 +137,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
   const int qi = q0 + 32 * w + l32;  // this lane's query
+  FragOffsets<D> fo;
+  fo.init(lane);
   const bool qvalid = qi < e;
 
   // ---- Q^T operand, resident for the whole kernel (rows past the document end read as zero)
@@ -209,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       // ahead of its use; the scheduling barriers keep that distance
       constexpr int PF = 2;
       auto kfrag = [&](int m) {
-        return *reinterpret_cast<const uint4*>(ks + S::L::off((m / KK) * 32 + l32, 16 * (m % KK) + 8 * half));
+        return lds_ld16(ks, fo.row_frag(m / KK, m % KK));
       };
       uint4 kf[PF + 1];
 #pragma unroll
@@ -284,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int st = 0; st < 2 * NB; ++st)
-          oacc[cb] = mfma32(a_from_rows<D>(vs, 16 * st, 32 * cb, lane), as_bf16x8(pb[st]), oacc[cb]);
+          oacc[cb] = mfma32(a_from_rows_at<D>(vs, fo, st, cb), as_bf16x8(pb[st]), oacc[cb]);
     }
 
     wait_vmem();

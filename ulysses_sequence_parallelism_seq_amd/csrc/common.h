@@ -129,9 +129,9 @@ template <int D>
 struct RowTile {
   static constexpr int RS = D;           // row stride (bf16 elements)
   static constexpr int CHUNKS = D / 8;   // 16-byte chunks per row
-  __device__ static __forceinline__ int chunk_key(int row) { return swz(row) & (CHUNKS - 1); }
+  __host__ __device__ static __forceinline__ int chunk_key(int row) { return swz(row) & (CHUNKS - 1); }
   // element offset of (row, col); col is a multiple of 4
-  __device__ static __forceinline__ int off(int row, int col) {
+  __host__ __device__ static __forceinline__ int off(int row, int col) {
     return row * RS + ((((col >> 3) ^ chunk_key(row)) << 3) | (col & 7));
   }
 };
@@ -181,6 +181,50 @@ __device__ __forceinline__ bf16x8 a_from_rows(const bf16* tile, int t0, int c0, 
   const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (p & 3);
   const uint2 lo = lds_read_tr16(tile + RowTile<D>::off(row, col));
   const uint2 hi = lds_read_tr16(tile + RowTile<D>::off(row + 8, col));
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Per-lane LDS byte offsets of the two fragment reads made from RowTile<D>
+// tiles, in a form that costs one register per pattern. Swizzle keys repeat
+// every 16 rows, and a chunk index x + y with x, y on disjoint bits, XORed with
+// a key, equals (y ^ key) ^ x; a row is 2D bytes with the chunk in bits 4 and
+// up, so each fragment's offset is a lane base XOR a constant, plus a constant
+// number of whole rows:
+//   * row operand (lane l: row 32 rb + l % 32, columns 16 kk + 8 h .. + 7),
+//     the operand RowTile::off reads for MFMAs with k along d:
+//     row_frag(rb, kk) = (row ^ (kk << 5)) + rb * 64 D;
+//   * transposing reads of a_from_rows for t0 = 16 j, c0 = 32 cb:
+//     (tr_lo or tr_hi) ^ (cb << 6), plus 32 D j.
+// Compilers keep offsets they cannot relate as separate registers; with these
+// the per-fragment offsets are a few XORs of three registers.
+template <int D>
+struct FragOffsets {
+  uint32_t row, tr_lo, tr_hi;
+  __host__ __device__ __forceinline__ void init(int lane) {
+    const int half = lane >> 5, l32 = lane & 31, p = lane & 15;
+    row = (uint32_t)(l32 * 2 * D) + ((uint32_t)(half ^ RowTile<D>::chunk_key(l32)) << 4);
+    const int r0 = 4 * half + (p >> 2);  // transposing reads: row of the low half
+    const int cl = 2 * ((lane >> 4) & 1) + ((p & 3) >> 1);
+    const uint32_t low = (uint32_t)(4 * (p & 1)) * 2u;  // bytes within the chunk
+    tr_lo = (uint32_t)(r0 * 2 * D) + ((uint32_t)(cl ^ RowTile<D>::chunk_key(r0)) << 4) + low;
+    tr_hi = (uint32_t)((r0 + 8) * 2 * D) + ((uint32_t)(cl ^ RowTile<D>::chunk_key(r0 + 8)) << 4) + low;
+  }
+  __host__ __device__ __forceinline__ uint32_t row_frag(int rb, int kk) const {
+    return (row ^ ((uint32_t)kk << 5)) + (uint32_t)(rb * 64 * D);
+  }
+};
+
+__device__ __forceinline__ uint4 lds_ld16(const void* tile, uint32_t byte_off) {
+  return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + byte_off);
+}
+
+// a_from_rows with the offsets of FragOffsets: t0 = 16 j, c0 = 32 cb.
+template <int D>
+__device__ __forceinline__ bf16x8 a_from_rows_at(const bf16* tile, const FragOffsets<D>& fo, int j, int cb) {
+  const char* t = reinterpret_cast<const char*>(tile) + j * 32 * D;
+  const uint32_t x = (uint32_t)cb << 6;
+  const uint2 lo = lds_read_tr16(reinterpret_cast<const bf16*>(t + (fo.tr_lo ^ x)));
+  const uint2 hi = lds_read_tr16(reinterpret_cast<const bf16*>(t + (fo.tr_hi ^ x)));
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
