@@ -537,59 +537,99 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
       const int qt0 = qlast - i * kKvBQ;
       // tiles that cross the diagonal or a document end are masked element by element
       const bool need_mask = (causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
+      // S = Q K^T and dP = dO V^T of both 32-query blocks. The exponentials of
+      // block 0 run between the MFMAs of block 1, four elements every other
+      // k-step (their lse2 and D read one step before), so the wave's own
+      // matrix work covers half of its softmax.
+      f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        f32x16 sacc, pacc;
+      for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sacc[x] = pacc[x] = 0.f;
-        // Q and dO fragments read two k-steps ahead of their MFMAs
-        auto rd = [&](int kk, uint4* f) {
-          const uint32_t off = fo.row_frag(qb, kk);
-          f[0] = lds_ld16(st.q, off);
-          f[1] = lds_ld16(st.dout, off);
-        };
-        uint4 fr[3][2];
-        rd(0, fr[0]);
-        rd(1, fr[1]);
+        for (int x = 0; x < 16; ++x) sacc[qb][x] = pacc[qb][x] = 0.f;
+      // Q and dO fragments read two k-steps ahead of their MFMAs
+      auto rd = [&](int qb, int kk, uint4* f) {
+        const uint32_t off = fo.row_frag(qb, kk);
+        f[0] = lds_ld16(st.q, off);
+        f[1] = lds_ld16(st.dout, off);
+      };
+      // lse2 and D of the four queries of accumulator elements 4 gq .. 4 gq + 3
+      auto rd_ld = [&](int qb, int gq, float4& l4, float4& d4) {
+        l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
+        d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
+      };
+      // in place: sacc becomes P, pacc becomes dP - D
+      auto soft4 = [&](int qb, int gq, const float4& l4, const float4& d4) {
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 2 < KK) rd(kk + 2, fr[(kk + 2) % 3]);
-          sacc = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc);
-          pacc = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int x = 0; x < 4; ++x) {
+          const int i2 = 4 * gq + x;
+          sacc[qb][i2] = fast_exp2(fmaf(sacc[qb][i2], a.sl2, -lv[x]));
+          pacc[qb][i2] = pacc[qb][i2] - dv[x];
         }
-        float p[16], ds[16];
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
-          const float4 d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
-          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-          const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            const int i2 = 4 * gq + x;
-            p[i2] = fast_exp2(fmaf(sacc[i2], a.sl2, -lv[x]));
-            ds[i2] = pacc[i2] - dv[x];
-          }
-        }
+      };
+      // masked P (zero where the key is not visible to the query) and P (dP - D)
+      // of accumulator elements 8 mm .. 8 mm + 7 of block qb, packed to bf16
+      auto pack8 = [&](int qb, int mm) {
+        const int b = 8 * mm;
         if (need_mask) {
 #pragma unroll
-          for (int x = 0; x < 16; ++x) {
+          for (int x = b; x < b + 8; ++x) {
             const int qq = qt0 + 32 * qb + 8 * (x >> 2) + 4 * half + (x & 3);
-            if (qq >= e || kj >= e || (causal && kj > qq)) p[x] = 0.f;
+            if (qq >= e || kj >= e || (causal && kj > qq)) sacc[qb][x] = 0.f;
           }
         }
+        const f32x16& p = sacc[qb];
+        const f32x16& ds = pacc[qb];
+        pk[4 * qb + mm] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
+                                     pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
+        pk[4 * qb + 2 + mm] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
+                                         pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
+                                         pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
+                                         pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
+      };
+      {
+        uint4 fr[3][2];
+        rd(0, 0, fr[0]);
+        rd(0, 1, fr[1]);
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const int b = 8 * mm;
-          pk[4 * qb + mm] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
-                                       pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
-          pk[4 * qb + 2 + mm] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
-                                           pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
-                                           pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
-                                           pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 2 < KK) rd(0, kk + 2, fr[(kk + 2) % 3]);
+          sacc[0] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[0]);
+          pacc[0] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[0]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
+      {
+        uint4 fr[3][2];
+        float4 l4, d4;
+        rd(1, 0, fr[0]);
+        rd(1, 1, fr[1]);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          if (kk + 2 < KK) rd(1, kk + 2, fr[(kk + 2) % 3]);
+          if ((kk & 1) == 0 && kk / 2 < 4) rd_ld(0, kk / 2, l4, d4);
+          sacc[1] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[1]);
+          pacc[1] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[1]);
+          if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2, l4, d4);
+          if (kk == 3 || kk == 7) pack8(0, kk / 4);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // with D = 64 there are only four k-steps: the rest of block 0 here
+#pragma unroll
+        for (int gq = KK / 2; gq < 4; ++gq) {
+          rd_ld(0, gq, l4, d4);
+          soft4(0, gq, l4, d4);
+        }
+        if (KK < 8) pack8(0, 1);
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          rd_ld(1, gq, l4, d4);
+          soft4(1, gq, l4, d4);
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < 2; ++mm) pack8(1, mm);
     };
     auto publish = [&](int i) {
       if (i >= ntiles) return;
