@@ -364,7 +364,8 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 //   * producer p: K^T and V^T of the 32 keys stay in registers as B operands;
 //     per tile it computes S = Q K^T and dP = dO V^T for both 32-query blocks
 //     (lane = key), then P = exp2(S * log2(e) / sqrt(d) - lse2) and
-//     dS = P (dP - D), packed to bf16 in the order the MFMA k index takes them;
+//     dS = P (dP - D), packed to bf16 in the order the MFMA k index takes them
+//     (query block 0's exponentials and packing run between block 1's MFMAs);
 //   * consumers, one tile behind: consumer c accumulates dV^T += dO^T P and
 //     dK^T += Q^T dS for the 64 keys of producers 2 (c/2) and 2 (c/2) + 1 and
 //     half of the D columns, with the A operands read transposed from the
