@@ -168,22 +168,6 @@ struct TileDma {
   }
 };
 
-// MFMA A operand (rows = 32 columns c0 .. c0+31 of a [token][d] LDS tile in
-// the RowTile layout; k = 16 tokens from t0) read with two transposing
-// reads. Lane l (h = l / 32) receives column c0 + l % 32 of tokens
-// t0 + 4h + (0..3) and t0 + 8 + 4h + (0..3): MFMA k index 8h + j is token
-// t0 + 4h + j (j < 4) or t0 + 8 + 4h + (j - 4), the same token order as an
-// accumulator's rows.
-template <int D>
-__device__ __forceinline__ bf16x8 a_from_rows(const bf16* tile, int t0, int c0, int lane) {
-  const int p = lane & 15;
-  const int row = t0 + 4 * (lane >> 5) + (p >> 2);
-  const int col = c0 + 16 * ((lane >> 4) & 1) + 4 * (p & 3);
-  const uint2 lo = lds_read_tr16(tile + RowTile<D>::off(row, col));
-  const uint2 hi = lds_read_tr16(tile + RowTile<D>::off(row + 8, col));
-  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
-}
-
 // Per-lane LDS byte offsets of the two fragment reads made from RowTile<D>
 // tiles, in a form that costs one register per pattern. Swizzle keys repeat
 // every 16 rows, and a chunk index x + y with x, y on disjoint bits, XORed with
@@ -193,7 +177,9 @@ __device__ __forceinline__ bf16x8 a_from_rows(const bf16* tile, int t0, int c0, 
 //   * row operand (lane l: row 32 rb + l % 32, columns 16 kk + 8 h .. + 7),
 //     the operand RowTile::off reads for MFMAs with k along d:
 //     row_frag(rb, kk) = (row ^ (kk << 5)) + rb * 64 D;
-//   * transposing reads of a_from_rows for t0 = 16 j, c0 = 32 cb:
+//   * the two transposing reads of a_from_rows_at (t0 = 16 j, c0 = 32 cb),
+//     whose lane l reads row t0 + 4 (l / 32) + (l % 16) / 4 (+ 8 for the
+//     second) at column c0 + 16 ((l / 16) % 2) + 4 (l % 4):
 //     (tr_lo or tr_hi) ^ (cb << 6), plus 32 D j.
 // Compilers keep offsets they cannot relate as separate registers; with these
 // the per-fragment offsets are a few XORs of three registers.
@@ -218,7 +204,12 @@ __device__ __forceinline__ uint4 lds_ld16(const void* tile, uint32_t byte_off) {
   return *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(tile) + byte_off);
 }
 
-// a_from_rows with the offsets of FragOffsets: t0 = 16 j, c0 = 32 cb.
+// MFMA A operand (rows = 32 columns c0 .. c0+31 of a [token][d] LDS tile in
+// the RowTile layout; k = 16 tokens from t0), t0 = 16 j and c0 = 32 cb, read
+// with two transposing reads at the offsets of FragOffsets. Lane l
+// (h = l / 32) receives column c0 + l % 32 of tokens t0 + 4h + (0..3) and
+// t0 + 8 + 4h + (0..3): MFMA k index 8h + i is token t0 + 4h + i (i < 4) or
+// t0 + 8 + 4h + (i - 4), the same token order as an accumulator's rows.
 template <int D>
 __device__ __forceinline__ bf16x8 a_from_rows_at(const bf16* tile, const FragOffsets<D>& fo, int j, int cb) {
   const char* t = reinterpret_cast<const char*>(tile) + j * 32 * D;

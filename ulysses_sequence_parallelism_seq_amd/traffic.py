@@ -4,8 +4,9 @@ Two counter runs of bench.py (one with FETCH_SIZE, one with WRITE_SIZE, in
 KiB per dispatch) give the bytes each kernel moved between L2 and memory. The
 counters are calibrated with the permute kernel of the same run, a plain copy
 whose bytes are known (it reads and writes every element once), and the
-figures are stored with a hash of the kernel sources so a later change of the
-kernels invalidates them.
+figures are stored with a hash of the compiled library they were taken with,
+so that any change of its code invalidates them (and an edit that leaves the
+compiled code byte-identical, such as a comment, does not).
 
   python -m ulysses_sequence_parallelism_seq_amd.traffic FETCH_DIR WRITE_DIR OUT.txt "COMMANDS"
 
@@ -22,16 +23,19 @@ import os
 import sys
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-SOURCES = ["csrc/attn_bwd.hip", "csrc/common.h", "csrc/permute.hip"]
+LIBRARY = os.path.join(_HERE, "libulysses.so")
 BWD_KERNELS = ("attn_dkdv_bf16_kernel<128,false>", "attn_dq_bf16_kernel<128,false>", "delta_bf16_kernel<128>")
 COPY_KERNEL = "permute_seq_to_head"
 
 
-def sources_sha256() -> str:
+def library_sha256() -> str | None:
+    """sha256 of the built library, or None if it has not been built."""
+    if not os.path.exists(LIBRARY):
+        return None
     h = hashlib.sha256()
-    for rel in SOURCES:
-        with open(os.path.join(_HERE, rel), "rb") as f:
-            h.update(f.read())
+    with open(LIBRARY, "rb") as f:
+        for block in iter(lambda: f.read(1 << 20), b""):
+            h.update(block)
     return h.hexdigest()
 
 
@@ -62,7 +66,7 @@ def write_traffic(fetch_dir: str, write_dir: str, out: str, commands: str, copy_
     lines = [
         "# HBM traffic per dispatch (rocprofv3 FETCH_SIZE / WRITE_SIZE, KiB), long workload",
         f"# commands: {commands}",
-        f"source_sha256 {sources_sha256()}",
+        f"library_sha256 {library_sha256()}",
         f"copy {COPY_KERNEL} bytes={copy_bytes} fetch_kib={fetch[COPY_KERNEL]:.1f} write_kib={write[COPY_KERNEL]:.1f}",
     ]
     for k in BWD_KERNELS:
@@ -81,11 +85,11 @@ def read_traffic(path: str):
             parts = line.split()
             if not parts or parts[0].startswith("#"):
                 continue
-            if parts[0] == "source_sha256":
+            if parts[0] == "library_sha256":
                 rec["sha"] = parts[1]
             elif parts[0] in ("copy", "kernel"):
                 rec[(parts[0], parts[1])] = dict(p.split("=") for p in parts[2:])
-    if rec.get("sha") != sources_sha256():
+    if rec.get("sha") is None or rec.get("sha") != library_sha256():
         return None
     entries = [(k, v) for k, v in rec.items() if isinstance(k, tuple)]
     copy = next(v for (kind, _), v in entries if kind == "copy")
