@@ -49,7 +49,7 @@ struct BwdArgs {
   const bf16* o;
   const bf16* dout;
   const float* lse;
-  float* delta;  // workspace: D, then lse in log2 units (units * N floats each)
+  float* delta;  // workspace: -D, then lse in log2 units (units * N floats each)
   float* lse2;
   bf16* dq;
   bf16* dk;
@@ -104,7 +104,9 @@ __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int
 }
 
 // ------------------------------------------------------------------ D pre-pass
-// D[unit][t] = sum_c dO[t][c] * O[t][c]; D/8 lanes per row, 16 bytes per lane.
+// D[unit][t] = sum_c dO[t][c] * O[t][c], stored negated (the dK/dV kernel
+// starts its dP accumulators from it, so its MFMAs leave dP - D); D/8 lanes
+// per row, 16 bytes per lane.
 // Also lse2[unit][t] = lse[unit][t] * log2(e), the form the dK/dV kernel stages.
 // blockIdx.y = unit (g * Hl + h), blockIdx.x = a span of kDeltaPasses * 256 / (D/8)
 // tokens; each group of D/8 lanes takes kDeltaPasses rows, all loads (non-temporal:
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
       for (int m = LPR / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 64);
       if (t < N && sub == 0) {
         const size_t row = (size_t)unit * N + t;
-        delta[row] = acc;
+        delta[row] = -acc;
         lse2[row] = lse[row] * kLog2e;
       }
     }
@@ -239,7 +241,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
     }
   }
   const float lse2 = qvalid ? a.lse[(size_t)unit * a.N + qi] * kLog2e : 0.f;
-  const float dlt = qvalid ? a.delta[(size_t)unit * a.N + qi] : 0.f;
+  const float ndlt = qvalid ? a.delta[(size_t)unit * a.N + qi] : 0.f;  // -D
 
   const int kend = causal ? min(e, q0 + kDqBQ) : e;
   const int ntiles = (kend - s + kDqBK - 1) / kDqBK;
@@ -315,7 +317,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int i = 8 * mm + j;
-            ds[j] = fast_exp2(fmaf(sacc[i], a.sl2, -lse2)) * (pacc[i] - dlt);
+            ds[j] = fast_exp2(fmaf(sacc[i], a.sl2, -lse2)) * (pacc[i] + ndlt);
           }
           dsb[mm] = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
                                pack_bf16x2(ds[6], ds[7]));
@@ -386,7 +388,7 @@ struct KvStage {
   bf16 q[kKvBQ * D];     // RowTile layout
   bf16 dout[kKvBQ * D];  // RowTile layout
   float lse2[kKvBQ];
-  float dlt[kKvBQ];
+  float dlt[kKvBQ];  // -D
 };
 
 // Direct-to-LDS loads of one query tile: the 2 * kKvBQ rows of Q and dO are
@@ -542,31 +544,38 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
       // block 0 run between the MFMAs of block 1, four elements every other
       // k-step (their lse2 and D read one step before), so the wave's own
       // matrix work covers half of its softmax.
+      // dP starts from -D of its queries (the pre-pass stores D negated), so
+      // the MFMAs leave dP - D and the softmax has no subtraction to do
       f32x16 sacc[2], pacc[2];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
+      for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
-        for (int x = 0; x < 16; ++x) sacc[qb][x] = pacc[qb][x] = 0.f;
+        for (int gq = 0; gq < 4; ++gq) {
+          const float4 d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
+          sacc[qb][4 * gq] = sacc[qb][4 * gq + 1] = sacc[qb][4 * gq + 2] = sacc[qb][4 * gq + 3] = 0.f;
+          pacc[qb][4 * gq] = d4.x;
+          pacc[qb][4 * gq + 1] = d4.y;
+          pacc[qb][4 * gq + 2] = d4.z;
+          pacc[qb][4 * gq + 3] = d4.w;
+        }
+      }
       // Q and dO fragments read two k-steps ahead of their MFMAs
       auto rd = [&](int qb, int kk, uint4* f) {
         const uint32_t off = fo.row_frag(qb, kk);
         f[0] = lds_ld16(st.q, off);
         f[1] = lds_ld16(st.dout, off);
       };
-      // lse2 and D of the four queries of accumulator elements 4 gq .. 4 gq + 3
-      auto rd_ld = [&](int qb, int gq, float4& l4, float4& d4) {
+      // lse2 of the four queries of accumulator elements 4 gq .. 4 gq + 3
+      auto rd_ld = [&](int qb, int gq, float4& l4) {
         l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
-        d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
       };
-      // in place: sacc becomes P, pacc becomes dP - D
-      auto soft4 = [&](int qb, int gq, const float4& l4, const float4& d4) {
+      // in place: sacc becomes P
+      auto soft4 = [&](int qb, int gq, const float4& l4) {
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int x = 0; x < 4; ++x) {
           const int i2 = 4 * gq + x;
           sacc[qb][i2] = fast_exp2(fmaf(sacc[qb][i2], a.sl2, -lv[x]));
-          pacc[qb][i2] = pacc[qb][i2] - dv[x];
         }
       };
       // masked P (zero where the key is not visible to the query) and P (dP - D)
@@ -603,30 +612,30 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
       }
       {
         uint4 fr[3][2];
-        float4 l4, d4;
+        float4 l4;
         rd(1, 0, fr[0]);
         rd(1, 1, fr[1]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           if (kk + 2 < KK) rd(1, kk + 2, fr[(kk + 2) % 3]);
-          if ((kk & 1) == 0 && kk / 2 < 4) rd_ld(0, kk / 2, l4, d4);
+          if ((kk & 1) == 0 && kk / 2 < 4) rd_ld(0, kk / 2, l4);
           sacc[1] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[1]);
           pacc[1] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[1]);
-          if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2, l4, d4);
+          if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2, l4);
           if (kk == 3 || kk == 7) pack8(0, kk / 4);
           __builtin_amdgcn_sched_barrier(0);
         }
         // with D = 64 there are only four k-steps: the rest of block 0 here
 #pragma unroll
         for (int gq = KK / 2; gq < 4; ++gq) {
-          rd_ld(0, gq, l4, d4);
-          soft4(0, gq, l4, d4);
+          rd_ld(0, gq, l4);
+          soft4(0, gq, l4);
         }
         if (KK < 8) pack8(0, 1);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          rd_ld(1, gq, l4, d4);
-          soft4(1, gq, l4, d4);
+          rd_ld(1, gq, l4);
+          soft4(1, gq, l4);
         }
       }
 #pragma unroll
@@ -860,7 +869,7 @@ int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void
 extern "C" size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype) {
   if (sp <= 0 || B <= 0 || N <= 0 || Hl <= 0) return 0;
   if (!uly_host::dtype_ok(dtype) || !uly_host::head_dim_ok(d)) return 0;
-  // D = rowsum(dO * O) and lse in log2 units: two floats per (rank, batch row, head, token).
+  // -D = -rowsum(dO * O) and lse in log2 units: two floats per (rank, batch row, head, token).
   return 2 * (size_t)sp * B * Hl * N * sizeof(float);
 }
 
