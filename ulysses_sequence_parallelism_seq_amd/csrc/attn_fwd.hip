@@ -17,7 +17,7 @@
 //     holds one query and 16 keys, so row max and row sum are in-register
 //     except for one exchange between the two half-waves.
 //   * Online softmax in the exp2 domain (log2(e)/sqrt(d) folded into the
-//     exponent's FMA), with a lazily moved running max (see kRescaleSlack). P^T is packed to bf16 straight from the accumulator and is
+//     exponent's FMA), with a lazily moved running max (see kSumLimit). P^T is packed to bf16 straight from the accumulator and is
 //     the B operand of O^T += V^T P^T, again a 32x32x16 MFMA, whose A
 //     operand V^T comes from the row-major V tile through gfx950's
 //     transposing LDS reads. The MFMA k index is mapped to keys so that each
@@ -80,12 +80,13 @@ struct FwdArgs {
   int step, sp, B;
 };
 
-// Lazy rescale: the running max used in the exponentials only moves when a
-// row's new maximum exceeds it by more than 8 (log2 units). The O accumulator
-// is then rescaled rarely, and P = exp2(x - m) stays below 2^8, which fp32
-// sums and bf16 MFMA operands hold as exactly as values below 1; the final
-// normalisation uses the same m, so the result is unchanged.
-constexpr float kRescaleSlack = 8.0f;
+// Lazy rescale: the running max m used in the exponentials only moves when
+// a tile's row sum of exp2(x - m) would reach 2^64 (or overflow, as on a
+// row's first keys, where m is not set yet). Until then P may exceed 1 by
+// that much, which fp32 sums, fp32 accumulators and bf16 MFMA operands hold
+// with the same relative precision; the final normalisation uses the same m,
+// so the result is the same softmax. Most tiles thus need no row max at all.
+constexpr float kSumLimit = 0x1p64f;
 
 // kRing: one step of ring attention. Row g = r * B + b holds rank r's query
 // chunk; its keys and values come from chunk j = (r - step) mod sp, the whole
@@ -224,31 +225,46 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       // mask where the tile crosses the diagonal or the document end (scale applied in the exponent)
       const bool need_mask = (causal && kt0 + kBK - 1 > q0) || kt0 + kBK > e;
-      float mloc = -INFINITY;
       if (need_mask) {
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            float x = sacc[blk][i];
             const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= e || (causal && key > qi)) x = -INFINITY;
-            sacc[blk][i] = x;
-            mloc = fmaxf(mloc, x);
+            if (key >= e || (causal && key > qi)) sacc[blk][i] = -INFINITY;
           }
-      } else {
+      }
+
+      // P^T = exp2(x - m) against the current running max m, optimistically:
+      // the tile's row sum shows whether m has fallen too far behind (or, on
+      // a row's first keys, was never set). Only then is the tile's row max
+      // taken (over both half-waves, which hold different keys of the same
+      // query), O and the running sum rescaled and the exponentials redone.
+      // The row sum takes the tile's 32 values pairwise before adding them to
+      // the running sum: over a long row that adds far fewer roundings than
+      // one value at a time (which matters when many terms are alike).
+      static_assert(NB == 2, "the pairwise tile sum covers four groups of eight");
+      float p[NB][16];
+      auto exps = [&]() {
+        float ls[2 * NB];
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            mloc = fmaxf(mloc, sacc[blk][i]);
+          for (int mm = 0; mm < 2; ++mm) {
+            float* q8 = &p[blk][8 * mm];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) q8[j] = fast_exp2(fmaf(sacc[blk][8 * mm + j], a.sl2, -m_run));
+            ls[blk * 2 + mm] = ((q8[0] + q8[1]) + (q8[2] + q8[3])) + ((q8[4] + q8[5]) + (q8[6] + q8[7]));
           }
-      }
-      // The two half-waves hold different keys of the same queries. Whether
-      // the running max must move is decided on each half's own maximum (the
-      // row max clears the slack iff one of the halves does); the row max
-      // itself, which needs an exchange between the halves, only when it moves.
-      if (__any(mloc * a.sl2 > m_run + kRescaleSlack)) {
+        return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      };
+      float lt = exps();
+      if (__any(!(lt < kSumLimit))) {
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < NB; ++blk)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sacc[blk][i]);
         const float m_new = fmaxf(m_run, fmaxf(mloc, swap_halves(mloc)) * a.sl2);
         const float alpha = fast_exp2(m_run - m_new);
         m_run = m_new;
@@ -257,27 +273,19 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) oacc[cb][i] *= alpha;
+        lt = exps();
       }
-
-      // P^T = exp2(x - m), packed to bf16 as the B operand of four 16-key MFMA
-      // steps. The row sum takes the tile's 32 values pairwise before adding
-      // them to the running sum: over a long row that adds far fewer roundings
-      // than one value at a time (which matters when many terms are alike).
-      static_assert(NB == 2, "the pairwise tile sum covers four groups of eight");
+      l_run += lt;
+      // packed to bf16 as the B operand of four 16-key MFMA steps
       uint4 pb[2 * NB];
-      float ls[2 * NB];
 #pragma unroll
       for (int blk = 0; blk < NB; ++blk)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) p[j] = fast_exp2(fmaf(sacc[blk][8 * mm + j], a.sl2, -m_run));
-          ls[blk * 2 + mm] = ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-          pb[blk * 2 + mm] = make_uint4(pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7]));
+          const float* q8 = &p[blk][8 * mm];
+          pb[blk * 2 + mm] = make_uint4(pack_bf16x2(q8[0], q8[1]), pack_bf16x2(q8[2], q8[3]),
+                                        pack_bf16x2(q8[4], q8[5]), pack_bf16x2(q8[6], q8[7]));
         }
-      l_run += (ls[0] + ls[1]) + (ls[2] + ls[3]);
 
       // O^T += V^T P^T: the A operand is V^T read from the row-major V tile
       // with transposing reads; step (blk, mm) covers keys blk*32 + 16*mm ..
