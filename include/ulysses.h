@@ -108,8 +108,8 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * Bytes of device workspace ulysses_attn_bwd needs: two floats per (rank,
- * batch row, head, token) (the row sums D = rowsum(dO * O) and lse in log2
- * units, both stored negated), i.e. O(N), never O(N^2). Returns 0 for invalid arguments.
+ * batch row, head, token) (the row sums D = rowsum(dO * O), stored negated,
+ * and lse in log2 units), i.e. O(N), never O(N^2). Returns 0 for invalid arguments.
  */
 size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype);
 
@@ -167,13 +167,13 @@ int ulysses_ring_attn_fwd_step(const void* q, const void* k, const void* v, void
 
 /*
  * Bytes of workspace the ring backward needs: two floats per (rank, batch
- * row, head, token) (-D = -rowsum(dO * O) and -lse in log2 units). Returns
- * 0 for invalid arguments.
+ * row, head, token) (-D = -rowsum(dO * O) and lse in log2 units). Returns 0
+ * for invalid arguments.
  */
 size_t ulysses_ring_attn_bwd_workspace_bytes(int sp, int B, int Ns, int H, int d, int dtype);
 
 /*
- * Before the backward steps: -D = -rowsum(dO * O) and -lse * log2(e) of every
+ * Before the backward steps: -D = -rowsum(dO * O) and lse * log2(e) of every
  * query row into the workspace, from the forward's final o and lse.
  *   o, dout [sp][B][Ns][H][d] bf16; lse [sp][B][H][Ns] float.
  * Errors: as ulysses_ring_attn_fwd_step, plus ULY_EWORKSPACE.

@@ -185,3 +185,26 @@ def test_bf16_constant_v_and_zero_q():
     assert_rel(o[0, 0, :, 0], want, TOL_BF16_O, "O q=0")
     np.testing.assert_allclose(f64(lse)[0, 0, 0], np.log(np.arange(1, N + 1)), atol=1e-4)
     assert torch.count_nonzero(dk) == 0
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_bf16_rising_scores(causal):
+    """Scores that climb by about 25 log2 units per 64-key tile along every
+    row (keys scaled by a ramp): the forward's running max falls far behind
+    and is moved many times by the overflow check of a tile's row sum, with
+    weights up to 2^64 before each move. Same softmax as the oracle's."""
+    say("bf16 rising scores", causal)
+    N, d = 1024, 128
+    base = workloads.qkv_do((1, 1, N, 2, d), 91, "fp32")
+    ramp = (50.0 * torch.arange(N, dtype=torch.float32) / N).view(1, 1, N, 1, 1)
+    q = (0.5 + 0.1 * base[0]).to(torch.bfloat16)
+    k = (ramp * (1.0 + 0.1 * base[1])).to(torch.bfloat16)
+    v = base[2].to(torch.bfloat16)
+    do = base[3].to(torch.bfloat16)
+    o, lse, dq, dk, dv = _run_gpu(q, k, v, do, None, causal)
+    O, L = oracle.attn_fwd(q, k, v, None, causal)
+    G = oracle.attn_bwd(q, k, v, do, None, causal)
+    assert_rel(o, O, TOL_BF16_O, "O")
+    assert_abs(lse, L, 1e-3, "lse")
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), G):
+        assert_rel(got, want, TOL_BF16_GRAD, name)

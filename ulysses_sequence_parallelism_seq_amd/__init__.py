@@ -272,7 +272,7 @@ def ulysses_ring_attn_bwd_workspace_bytes(sp: int, B: int, Ns: int, H: int, d: i
 
 
 def ulysses_ring_attn_bwd_prepare(o, dout, lse, workspace=None):
-    """-D = -rowsum(dO * O) and -lse * log2(e) into the (returned) workspace."""
+    """-D = -rowsum(dO * O) and lse * log2(e) into the (returned) workspace."""
     sp, B, Ns, H, d = _ring_shape(o)
     if dout.shape != o.shape or dout.dtype != o.dtype:
         raise ValueError("o and dout must share shape and dtype")

@@ -49,7 +49,7 @@ struct BwdArgs {
   const bf16* o;
   const bf16* dout;
   const float* lse;
-  float* delta;  // workspace: -D, then -lse in log2 units (units * N floats each)
+  float* delta;  // workspace: -D, then lse in log2 units (units * N floats each)
   float* lse2;
   bf16* dq;
   bf16* dk;
@@ -107,7 +107,7 @@ __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int
 // D[unit][t] = sum_c dO[t][c] * O[t][c], stored negated (the dK/dV kernel
 // starts its dP accumulators from it, so its MFMAs leave dP - D); D/8 lanes
 // per row, 16 bytes per lane.
-// Also nlse2[unit][t] = -lse[unit][t] * log2(e), the form the dK/dV kernel stages.
+// Also lse2[unit][t] = lse[unit][t] * log2(e), the form the dK/dV kernel stages.
 // blockIdx.y = unit (g * Hl + h), blockIdx.x = a span of kDeltaPasses * 256 / (D/8)
 // tokens; each group of D/8 lanes takes kDeltaPasses rows, all loads (non-temporal:
 // O and dO stream through once) issued before the first product.
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
       if (t < N && sub == 0) {
         const size_t row = (size_t)unit * N + t;
         delta[row] = -acc;
-        lse2[row] = -lse[row] * kLog2e;
+        lse2[row] = lse[row] * kLog2e;
       }
     }
   }
@@ -365,8 +365,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 // (waves p and p + 4) and 32 keys:
 //   * producer p: K^T and V^T of the 32 keys stay in registers as B operands;
 //     per tile it computes S = Q K^T and dP = dO V^T for both 32-query blocks
-//     (lane = key; K pre-scaled by log2(e) / sqrt(d), the accumulators
-//     starting from -lse2 and -D), then P = exp2(S * log2(e) / sqrt(d) - lse2) and
+//     (lane = key), then P = exp2(S * log2(e) / sqrt(d) - lse2) and
 //     dS = P (dP - D), packed to bf16 in the order the MFMA k index takes them
 //     (query block 0's exponentials and packing run between block 1's MFMAs);
 //   * consumers, one tile behind: consumer c accumulates dV^T += dO^T P and
@@ -388,7 +387,7 @@ template <int D>
 struct KvStage {
   bf16 q[kKvBQ * D];     // RowTile layout
   bf16 dout[kKvBQ * D];  // RowTile layout
-  float lse2[kKvBQ];  // -lse * log2(e)
+  float lse2[kKvBQ];
   float dlt[kKvBQ];  // -D
 };
 
@@ -532,15 +531,6 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
         kreg[kk] = buf_load16(kr, off + 32u * kk);
         vreg[kk] = buf_load16(vr, off + 32u * kk);
       }
-      // K pre-scaled by log2(e) / sqrt(d) (rounded to bf16 again): S comes out
-      // of the MFMAs in log2 units, ready for exp2
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        uint32_t* w4 = reinterpret_cast<uint32_t*>(&kreg[kk]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          w4[j] = pack_bf16x2(bf16_bits_to_float(w4[j] & 0xffffu) * a.sl2, bf16_bits_to_float(w4[j] >> 16) * a.sl2);
-      }
     }
     // P and dS of both query blocks as MFMA B operands: pk[4 qb + mm] = P,
     // pk[4 qb + 2 + mm] = dS, accumulator elements 8 mm .. 8 mm + 7
@@ -552,21 +542,17 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
       const bool need_mask = (causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
       // S = Q K^T and dP = dO V^T of both 32-query blocks. The exponentials of
       // block 0 run between the MFMAs of block 1, four elements every other
-      // k-step, so the wave's own matrix work covers half of its softmax.
-      // S starts from -lse2 and dP from -D of its queries (the pre-pass stores
-      // both negated), so the MFMAs leave S * log2(e) / sqrt(d) - lse2 (K is
-      // pre-scaled) and dP - D: P is one exp2 per element, dS one product
+      // k-step (their lse2 and D read one step before), so the wave's own
+      // matrix work covers half of its softmax.
+      // dP starts from -D of its queries (the pre-pass stores D negated), so
+      // the MFMAs leave dP - D and the softmax has no subtraction to do
       f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const float4 l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
           const float4 d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
-          sacc[qb][4 * gq] = l4.x;
-          sacc[qb][4 * gq + 1] = l4.y;
-          sacc[qb][4 * gq + 2] = l4.z;
-          sacc[qb][4 * gq + 3] = l4.w;
+          sacc[qb][4 * gq] = sacc[qb][4 * gq + 1] = sacc[qb][4 * gq + 2] = sacc[qb][4 * gq + 3] = 0.f;
           pacc[qb][4 * gq] = d4.x;
           pacc[qb][4 * gq + 1] = d4.y;
           pacc[qb][4 * gq + 2] = d4.z;
@@ -579,10 +565,18 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
         f[0] = lds_ld16(st.q, off);
         f[1] = lds_ld16(st.dout, off);
       };
-      // in place: sacc becomes P for accumulator elements 4 gq .. 4 gq + 3
-      auto soft4 = [&](int qb, int gq) {
+      // lse2 of the four queries of accumulator elements 4 gq .. 4 gq + 3
+      auto rd_ld = [&](int qb, int gq, float4& l4) {
+        l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
+      };
+      // in place: sacc becomes P
+      auto soft4 = [&](int qb, int gq, const float4& l4) {
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-        for (int x = 0; x < 4; ++x) sacc[qb][4 * gq + x] = fast_exp2(sacc[qb][4 * gq + x]);
+        for (int x = 0; x < 4; ++x) {
+          const int i2 = 4 * gq + x;
+          sacc[qb][i2] = fast_exp2(fmaf(sacc[qb][i2], a.sl2, -lv[x]));
+        }
       };
       // masked P (zero where the key is not visible to the query) and P (dP - D)
       // of accumulator elements 8 mm .. 8 mm + 7 of block qb, packed to bf16
@@ -618,26 +612,30 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
       }
       {
         uint4 fr[3][2];
+        float4 l4;
         rd(1, 0, fr[0]);
         rd(1, 1, fr[1]);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           if (kk + 2 < KK) rd(1, kk + 2, fr[(kk + 2) % 3]);
+          if ((kk & 1) == 0 && kk / 2 < 4) rd_ld(0, kk / 2, l4);
           sacc[1] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[1]);
           pacc[1] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[1]);
-          if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2);
+          if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2, l4);
           if (kk == 3 || kk == 7) pack8(0, kk / 4);
           __builtin_amdgcn_sched_barrier(0);
         }
         // with D = 64 there are only four k-steps: the rest of block 0 here
 #pragma unroll
         for (int gq = KK / 2; gq < 4; ++gq) {
-          soft4(0, gq);
+          rd_ld(0, gq, l4);
+          soft4(0, gq, l4);
         }
         if (KK < 8) pack8(0, 1);
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          soft4(1, gq);
+          rd_ld(1, gq, l4);
+          soft4(1, gq, l4);
         }
       }
 #pragma unroll
