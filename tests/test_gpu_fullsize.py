@@ -1,7 +1,10 @@
 """GPU parity at the workloads' full sizes, in the launch configuration the
 benchmark times: sampled outputs the oracle computes one by one, the q = 0
-closed forms over every row, and bit-exact permutes checked on sampled tokens
-plus a full round trip."""
+and uniform-row closed forms over every row and key, and bit-exact permutes
+checked on sampled tokens plus a full round trip. Besides the per-tensor
+bars, every compared row is held to a bar relative to its own size
+(row_rel_err), so late rows of long sequences, whose values are hundreds of
+times smaller than the first rows', are checked too."""
 
 from __future__ import annotations
 
@@ -13,7 +16,8 @@ import oracle
 import workloads
 import ulysses_sequence_parallelism_seq_amd as uly
 from tests import closed_forms as cf
-from tests.gpu_util import TOL_BF16_GRAD, TOL_BF16_O, assert_rel, device, f64, rel_err, say
+from tests.gpu_util import (ROW_TOL_GRAD, ROW_TOL_O, TOL_BF16_GRAD, TOL_BF16_O, assert_rel, assert_rows, device,
+                            dk_weights, dq_allowance, f64, rel_err, row_rel_err, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -55,6 +59,49 @@ def _gpu_fwd_bwd(q, k, v, do, cu):
     return out
 
 
+def _sampled(q1, k1, v1, do1, rows, cols, cu):
+    """Oracle values of sampled rows (O, lse, dQ) and key columns (dK, dV) of one
+    head, with the per-row allowances for dQ and dK (tests/gpu_util.py)."""
+    scale = 1.0 / np.sqrt(q1.shape[-1])
+    O_r, L_r = oracle.attn_fwd_rows(q1, k1, v1, rows, cu)
+    kbar, _ = oracle.attn_fwd_rows(q1, k1, k1, rows, cu)  # sum_j P_ij k_j
+    dq_r = oracle.attn_bwd_dq_rows(q1, k1, v1, do1, rows, cu)
+    dk_c, dv_c = oracle.attn_bwd_dkdv_cols(q1, k1, v1, do1, cols, cu)
+    # the allowance of key j sums over the queries that see it: the rows from the
+    # sampled columns to their document's end (causal)
+    cols_a = np.asarray(cols)
+    seen = []
+    for s, e in _bounds_of(cu, q1.shape[0]):
+        mine = cols_a[(cols_a >= s) & (cols_a < e)]
+        if mine.size:
+            seen.extend(range(int(mine.min()), e))
+    O_seen, _ = oracle.attn_fwd_rows(q1, k1, v1, seen, cu)
+    W = np.zeros(tuple(q1.shape), dtype=np.float64)
+    W[seen] = dk_weights(O_seen, f64(do1)[seen], f64(q1)[seen])[:, None]
+    _, ptw = oracle.attn_bwd_dkdv_cols(q1, k1, v1, W, cols, cu)  # sum_i P_ij w_i
+    return {"O": O_r, "dQ": dq_r, "dK": dk_c, "dV": dv_c, "lse": L_r,
+            "allow_dQ": dq_allowance(scale, kbar, O_r, f64(do1)[rows]), "allow_dK": scale * ptw[:, 0]}
+
+
+def _bounds_of(cu, N):
+    return [(0, N)] if cu is None else list(zip(np.asarray(cu)[:-1].tolist(), np.asarray(cu)[1:].tolist()))
+
+
+def _check_sampled(tag, got, want, allow, lse_err):
+    for n in got:
+        tol = TOL_BF16_O if n == "O" else TOL_BF16_GRAD
+        err = assert_rel(np.stack(got[n]), np.stack(want[n]), tol, f"{tag} {n}")
+        rtol = ROW_TOL_O if n == "O" else ROW_TOL_GRAD
+        a = np.concatenate(allow[n]) if n in allow else None
+        rerr = float(row_rel_err(np.stack(got[n]), np.stack(want[n]), a, rtol).max())
+        say(f"{tag} {n} rel err {err:.3e}, worst row {rerr:.3e}")
+    for n in got:
+        a = np.concatenate(allow[n]) if n in allow else None
+        assert_rows(np.stack(got[n]), np.stack(want[n]), ROW_TOL_O if n == "O" else ROW_TOL_GRAD, f"{tag} {n}", a)
+    say(f"{tag} lse max abs err {lse_err:.3e}")
+    assert lse_err < 1e-3
+
+
 @pytest.mark.parametrize("name", ["llama7b", "packed", "long", "million"])
 def test_fullsize_sampled_oracle(name):
     w = workloads.WORKLOADS[name]
@@ -67,27 +114,19 @@ def test_fullsize_sampled_oracle(name):
     cols = _end_cols(bounds, 48 if w.N > 40000 else 256)
     got = {n: [] for n in ("O", "dQ", "dK", "dV")}
     want = {n: [] for n in got}
+    allow = {"dQ": [], "dK": []}
     lse_err = 0.0
     for b in range(w.B):
         for h in range(w.Hl):
             sl = lambda t: t[0, b, :, h]  # noqa: E731
-            O_r, L_r = oracle.attn_fwd_rows(sl(q), sl(k), sl(v), rows, cu)
-            got["O"].append(f64(sl(o))[rows])
-            want["O"].append(O_r)
-            lse_err = max(lse_err, float(np.abs(f64(lse)[0, b, h, rows] - L_r).max()))
-            got["dQ"].append(f64(sl(dq))[rows])
-            want["dQ"].append(oracle.attn_bwd_dq_rows(sl(q), sl(k), sl(v), sl(do), rows, cu))
-            dk_c, dv_c = oracle.attn_bwd_dkdv_cols(sl(q), sl(k), sl(v), sl(do), cols, cu)
-            got["dK"].append(f64(sl(dk))[cols])
-            want["dK"].append(dk_c)
-            got["dV"].append(f64(sl(dv))[cols])
-            want["dV"].append(dv_c)
-    for n in got:
-        tol = TOL_BF16_O if n == "O" else TOL_BF16_GRAD
-        err = assert_rel(np.stack(got[n]), np.stack(want[n]), tol, f"{name} {n}")
-        say(f"{name} {n} rel err {err:.3e}")
-    say(f"{name} lse max abs err {lse_err:.3e}")
-    assert lse_err < 1e-3
+            ref = _sampled(sl(q), sl(k), sl(v), sl(do), rows, cols, cu)
+            lse_err = max(lse_err, float(np.abs(f64(lse)[0, b, h, rows] - ref["lse"]).max()))
+            for n, t, idx in (("O", o, rows), ("dQ", dq, rows), ("dK", dk, cols), ("dV", dv, cols)):
+                got[n].append(f64(sl(t))[idx])
+                want[n].append(ref[n])
+            allow["dQ"].append(ref["allow_dQ"])
+            allow["dK"].append(ref["allow_dK"])
+    _check_sampled(name, got, want, allow, lse_err)
 
 
 @pytest.mark.parametrize("name", ["llama7b", "packed"])
@@ -102,11 +141,18 @@ def test_fullsize_full_oracle_one_unit(name):
     one = lambda t: t[:, b:b + 1, :, h:h + 1]  # noqa: E731
     O, L = oracle.attn_fwd(one(q), one(k), one(v), cu)
     G = oracle.attn_bwd(one(q), one(k), one(v), one(do), cu)
+    scale = 1.0 / np.sqrt(w.d)
+    kbar, _ = oracle.attn_fwd(one(q), one(k), one(k), cu)  # sum_j P_ij k_j
+    W = np.broadcast_to(dk_weights(O, one(do), one(q)).reshape(O.shape[:-1])[..., None], O.shape)
+    ptw = oracle.attn_bwd(one(q), one(k), one(v), W, cu)[2][..., 0]  # sum_i P_ij w_i
+    allow = {"dQ": dq_allowance(scale, kbar, O, one(do)), "dK": scale * ptw, "dV": None}
     assert_rel(one(o), O, TOL_BF16_O, "O")
+    say(f"{name} O worst row {assert_rows(one(o), O, ROW_TOL_O, 'O'):.3e}")
     assert float(np.abs(f64(lse)[:, b:b + 1, h:h + 1] - L).max()) < 1e-3
     for n, got, want in zip(("dQ", "dK", "dV"), (one(dq), one(dk), one(dv)), G):
         err = assert_rel(got, want, TOL_BF16_GRAD, n)
-        say(f"{name} {n} rel err {err:.3e}")
+        rerr = assert_rows(got, want, ROW_TOL_GRAD, n, allow[n])
+        say(f"{name} {n} rel err {err:.3e}, worst row {rerr:.3e}")
 
 
 @pytest.mark.parametrize("name", ["packed", "long", "million"])
@@ -120,18 +166,75 @@ def test_fullsize_q0_closed_form(name):
     o, lse, dq, dk, dv = _gpu_fwd_bwd(q, k, v, do, cu)
     assert torch.count_nonzero(dk) == 0
     worst = {"O": 0.0, "dQ": 0.0, "dV": 0.0, "lse": 0.0}
+    rows = {"O": 0.0, "dQ": 0.0, "dV": 0.0}
     for b in range(w.B):
         for h in range(w.Hl):
             sl = lambda t: f64(t[0, b, :, h])  # noqa: E731
             O_c, L_c = cf.q0_forward(sl(v), cu)
             dq_c, _, dv_c = cf.q0_backward(sl(k), sl(v), sl(do), cu, block=512)
-            worst["O"] = max(worst["O"], rel_err(sl(o), O_c))
-            worst["dQ"] = max(worst["dQ"], rel_err(sl(dq), dq_c))
-            worst["dV"] = max(worst["dV"], rel_err(sl(dv), dv_c))
+            kbar, _ = cf.q0_forward(sl(k), cu)  # uniform P: the mean of the keys a query sees
+            allow = {"O": None, "dQ": dq_allowance(1.0 / np.sqrt(w.d), kbar, O_c, sl(do)), "dV": None}
+            for n, got, want in (("O", sl(o), O_c), ("dQ", sl(dq), dq_c), ("dV", sl(dv), dv_c)):
+                worst[n] = max(worst[n], rel_err(got, want))
+                rows[n] = max(rows[n], float(row_rel_err(got, want, allow[n], ROW_TOL_O if n == "O"
+                                                         else ROW_TOL_GRAD).max()))
             worst["lse"] = max(worst["lse"], float(np.abs(f64(lse)[0, b, h] - L_c).max()))
-    say(name, worst)
+    say(name, "per tensor", worst, "worst row", rows)
     assert worst["O"] <= TOL_BF16_O and worst["dQ"] <= TOL_BF16_GRAD and worst["dV"] <= TOL_BF16_GRAD
     assert worst["lse"] < 1e-3
+    assert rows["O"] <= ROW_TOL_O and rows["dQ"] <= ROW_TOL_GRAD and rows["dV"] <= ROW_TOL_GRAD, rows
+
+
+def uniform_allowances(q1, k1, v1, do1, O, cu, causal=True):
+    """dQ and dK row allowances (tests/gpu_util.py) when P is uniform over each
+    row: kbar_i is the mean of the keys query i sees, and sum_i P_ij w_i is the
+    dV closed form with dO replaced by w."""
+    scale = 1.0 / np.sqrt(q1.shape[-1])
+    kbar, _ = cf.q0_forward(k1, cu, causal)
+    W = np.broadcast_to(dk_weights(O, do1, q1)[:, None], q1.shape)
+    ptw = cf.q0_backward(k1, v1, W, cu, causal, block=512)[2][:, 0]
+    return {"dQ": dq_allowance(scale, kbar, O, do1), "dK": scale * ptw}
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("name", ["packed", "long", "million"])
+def test_fullsize_uniform_rows_closed_form(name):
+    """Queries orthogonal to the varying part of the keys (q_i = [a_i, 0], k_j =
+    [c, u_j]) give equal scores along each row, so every output has a closed
+    form: every row of O, lse and dQ and every key of dK and dV at full size,
+    with the dK/dV kernel's longest walks (every query tile of the document)
+    accumulating non-zero dS-weighted queries."""
+    w = workloads.WORKLOADS[name]
+    say("full-size uniform-row closed form", w)
+    cu, _ = _docs(w)
+    shape = (1, w.B, w.N, w.Hl, w.d)
+    ins = [torch.empty(shape, dtype=workloads.torch_dtype(w.dtype)) for _ in range(4)]
+    for b in range(w.B):
+        for h in range(w.Hl):
+            one = cf.uniform_inputs(w.N, w.d, 1000 * w.seed + 10 * b + h, w.scale)
+            for dst, x in zip(ins, one):
+                dst[0, b, :, h] = x.to(dst.dtype)
+    q, k, v, do = ins
+    o, lse, dq, dk, dv = _gpu_fwd_bwd(q, k, v, do, cu)
+    worst = {"O": 0.0, "dQ": 0.0, "dK": 0.0, "dV": 0.0, "lse": 0.0}
+    rows = {"O": 0.0, "dQ": 0.0, "dK": 0.0, "dV": 0.0}
+    for b in range(w.B):
+        for h in range(w.Hl):
+            sl = lambda t: f64(t[0, b, :, h])  # noqa: E731
+            O_c, L_c = cf.uniform_forward(sl(q), sl(k), sl(v), cu)
+            dq_c, dk_c, dv_c = cf.uniform_backward(sl(q), sl(k), sl(v), sl(do), cu, block=512)
+            allow = uniform_allowances(sl(q), sl(k), sl(v), sl(do), O_c, cu)
+            for n, got, want in (("O", sl(o), O_c), ("dQ", sl(dq), dq_c), ("dK", sl(dk), dk_c),
+                                 ("dV", sl(dv), dv_c)):
+                worst[n] = max(worst[n], rel_err(got, want))
+                rows[n] = max(rows[n], float(row_rel_err(got, want, allow.get(n), ROW_TOL_O if n == "O"
+                                                         else ROW_TOL_GRAD).max()))
+            worst["lse"] = max(worst["lse"], float(np.abs(f64(lse)[0, b, h] - L_c).max()))
+    say(name, "per tensor", worst, "worst row", rows)
+    assert worst["O"] <= TOL_BF16_O and worst["lse"] < 1e-3
+    assert max(worst["dQ"], worst["dK"], worst["dV"]) <= TOL_BF16_GRAD
+    assert rows["O"] <= ROW_TOL_O, rows
+    assert max(rows["dQ"], rows["dK"], rows["dV"]) <= ROW_TOL_GRAD, rows
 
 
 @pytest.mark.parametrize("name", ["long", "million"])
@@ -184,25 +287,17 @@ def test_bench_step_long_sampled():
     cols = _end_cols([(0, w.N)], 32)
     got = {n: [] for n in outs}
     want = {n: [] for n in outs}
+    allow = {"dQ": [], "dK": []}
     lse_err = 0.0
     for h in (0, 13, 31):  # virtual ranks 0, 3 and 7
         qh, kh, vh, doh = (full_head(x, h) for x in (q, k, v, do))
-        O_r, L_r = oracle.attn_fwd_rows(qh, kh, vh, rows)
-        got["O"].append(f64(full_head(outs["O"], h))[rows])
-        want["O"].append(O_r)
-        lse_err = max(lse_err, float(np.abs(f64(lse[h // w.Hl, 0, h % w.Hl].cpu())[rows] - L_r).max()))
-        got["dQ"].append(f64(full_head(outs["dQ"], h))[rows])
-        want["dQ"].append(oracle.attn_bwd_dq_rows(qh, kh, vh, doh, rows))
-        dk_c, dv_c = oracle.attn_bwd_dkdv_cols(qh, kh, vh, doh, cols)
-        got["dK"].append(f64(full_head(outs["dK"], h))[cols])
-        want["dK"].append(dk_c)
-        got["dV"].append(f64(full_head(outs["dV"], h))[cols])
-        want["dV"].append(dv_c)
+        ref = _sampled(qh, kh, vh, doh, rows, cols, None)
+        lse_err = max(lse_err, float(np.abs(f64(lse[h // w.Hl, 0, h % w.Hl].cpu())[rows] - ref["lse"]).max()))
+        for n, idx in (("O", rows), ("dQ", rows), ("dK", cols), ("dV", cols)):
+            got[n].append(f64(full_head(outs[n], h))[idx])
+            want[n].append(ref[n])
+        allow["dQ"].append(ref["allow_dQ"])
+        allow["dK"].append(ref["allow_dK"])
     del bufs
     torch.cuda.empty_cache()
-    for n in outs:
-        tol = TOL_BF16_O if n == "O" else TOL_BF16_GRAD
-        err = assert_rel(np.stack(got[n]), np.stack(want[n]), tol, f"bench step {n}")
-        say(f"bench step {n} rel err {err:.3e}")
-    say(f"bench step lse max abs err {lse_err:.3e}")
-    assert lse_err < 1e-3
+    _check_sampled("bench step", got, want, allow, lse_err)

@@ -11,8 +11,9 @@ import torch
 import oracle
 import workloads
 import ulysses_sequence_parallelism_seq_amd as uly
-from tests.gpu_util import (TOL_BF16_GRAD, TOL_BF16_O, TOL_F32_ABS, assert_abs, assert_rel, device, f64,
-                            say)
+from tests import closed_forms as cf
+from tests.gpu_util import (ROW_TOL_GRAD, ROW_TOL_O, TOL_BF16_GRAD, TOL_BF16_O, TOL_F32_ABS, assert_abs, assert_rel,
+                            assert_rows, device, dk_weights, dq_allowance, f64, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -140,6 +141,58 @@ def test_bf16_parity(sp, B, N, Hl, d, causal, lengths):
     assert_abs(lse, L, 1e-3, "lse")
     for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), G):
         assert_rel(got, want, TOL_BF16_GRAD, name)
+    # every row (token of one head) against its own size as well, with the
+    # allowances for dQ and dK that the stored O's rounding leaves (gpu_util)
+    rows = {"O": assert_rows(o, O, ROW_TOL_O, "O")}
+    for name, got, want, allow in zip(("dQ", "dK", "dV"), (dq, dk, dv), G, _grad_allowances(q, k, v, do, O, cu, causal)):
+        rows[name] = assert_rows(got, want, ROW_TOL_GRAD, name, allow)
+    say("worst rows", rows)
+
+
+def _grad_allowances(q, k, v, do, O, cu, causal):
+    """Per-row allowances of dQ (scale delta_i |kbar_i|) and dK (scale sum_i P_ij w_i)
+    from the oracle: the forward with v := k gives kbar_i = sum_j P_ij k_j, the
+    backward with dO := w gives sum_i P_ij w_i in its dV slot."""
+    scale = 1.0 / np.sqrt(q.shape[-1])
+    kbar, _ = oracle.attn_fwd(q, k, k, cu, causal)
+    W = np.broadcast_to(dk_weights(O, do, q).reshape(O.shape[:-1])[..., None], O.shape)
+    ptw = oracle.attn_bwd(q, k, v, W, cu, causal)[2][..., 0]
+    return dq_allowance(scale, kbar, O, do), scale * ptw, None
+
+
+@pytest.mark.parametrize("N,causal,lengths", [
+    (1000, True, None),
+    (777, False, [129, 128, 520]),
+    (900, True, [300, 0, 1, 64, 535]),
+])
+def test_bf16_uniform_rows(N, causal, lengths):
+    """Equal scores along each row (q_i = [a_i, 0], k_j = [c, u_j]): the GPU
+    against the hand-derived closed forms (pinned to the oracle on the CPU),
+    every row and key."""
+    say("bf16 uniform rows", N, causal, lengths)
+    cu = None if lengths is None else workloads.cu_seqlens_from_lengths(lengths)
+    ins = [torch.empty((1, 1, N, 2, 128), dtype=torch.bfloat16) for _ in range(4)]
+    for h in range(2):
+        for dst, x in zip(ins, cf.uniform_inputs(N, 128, 50 + h)):
+            dst[0, 0, :, h] = x.to(torch.bfloat16)
+    q, k, v, do = ins
+    o, lse, dq, dk, dv = _run_gpu(q, k, v, do, cu, causal)
+    for h in range(2):
+        sl = lambda t: f64(t[0, 0, :, h])  # noqa: E731
+        O_c, L_c = cf.uniform_forward(sl(q), sl(k), sl(v), cu, causal)
+        G_c = cf.uniform_backward(sl(q), sl(k), sl(v), sl(do), cu, causal, block=64)
+        assert_rel(sl(o), O_c, TOL_BF16_O, "O")
+        assert_rows(sl(o), O_c, ROW_TOL_O, "O")
+        assert_abs(f64(lse)[0, 0, h], L_c, 1e-3, "lse")
+        # uniform P: kbar_i is the mean of the keys query i sees; sum_i P_ij w_i the dV form with dO := w
+        scale = 1.0 / np.sqrt(128)
+        kbar, _ = cf.q0_forward(sl(k), cu, causal)
+        W = np.broadcast_to(dk_weights(O_c, sl(do), sl(q))[:, None], O_c.shape)
+        ptw = cf.q0_backward(sl(k), sl(v), W, cu, causal, block=64)[2][:, 0]
+        allow = (dq_allowance(scale, kbar, O_c, sl(do)), scale * ptw, None)
+        for name, got, want, a in zip(("dQ", "dK", "dV"), (dq, dk, dv), G_c, allow):
+            assert_rel(sl(got), want, TOL_BF16_GRAD, name)
+            assert_rows(sl(got), want, ROW_TOL_GRAD, name, a)
 
 
 def test_bf16_packed_equals_separate():

@@ -357,8 +357,37 @@ def check_backward_q0_closed_form():
                 np.testing.assert_allclose(dv[:, hh], cv, rtol=1e-12, atol=1e-13)
 
 
+def check_uniform_rows_closed_form():
+    """Queries orthogonal to the varying part of the keys: equal scores along
+    each row, so O, lse, dQ, dK and dV have the closed forms of
+    tests/closed_forms.py (dK non-zero, unlike q = 0)."""
+    N, H, d = 160, 2, 8
+    for causal in (True, False):
+        for lengths in (None, [33, 1, 0, 90, 36]):
+            cu = None if lengths is None else _lengths_to_cu(lengths)
+            ins = [np.zeros((N, H, d)) for _ in range(4)]
+            for hh in range(H):
+                for dst, x in zip(ins, cf.uniform_inputs(N, d, 17 + hh)):
+                    dst[:, hh] = x.numpy()
+            q, k, v, do = ins
+            O, LSE = oracle.attn_fwd(q, k, v, cu, causal)
+            grads = oracle.attn_bwd(q, k, v, do, cu, causal)
+            for hh in range(H):
+                Oc, Lc = cf.uniform_forward(q[:, hh], k[:, hh], v[:, hh], cu, causal)
+                np.testing.assert_allclose(O[:, hh], Oc, rtol=1e-12, atol=1e-12)
+                np.testing.assert_allclose(LSE[hh], Lc, rtol=1e-12, atol=1e-12)
+                gc = cf.uniform_backward(q[:, hh], k[:, hh], v[:, hh], do[:, hh], cu, causal, block=16)
+                for g, c in zip(grads, gc):
+                    assert np.abs(c).max() > 1e-2  # none of the three is trivially zero here
+                    np.testing.assert_allclose(g[:, hh], c, rtol=1e-10, atol=1e-12)
+
+
 def test_backward_finite_differences():
     check_backward_finite_differences()
+
+
+def test_uniform_rows_closed_form():
+    check_uniform_rows_closed_form()
 
 
 def test_backward_q0_closed_form():
@@ -430,6 +459,7 @@ PINS = [
     check_forward_vs_torch,
     check_backward_finite_differences,
     check_backward_q0_closed_form,
+    check_uniform_rows_closed_form,
 ]
 
 
