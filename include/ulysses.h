@@ -23,9 +23,10 @@
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is device memory owned by the caller, contiguous
- *     and row-major in the layout stated at the call. The library keeps no
- *     state, allocates no memory, and is safe to call from several host
- *     threads on different streams.
+ *     and row-major in the layout stated at the call. The library allocates
+ *     no memory and keeps no state, except the fixed per-GPU scratch of
+ *     ulysses_attn_bwd_noalloc (see there); every other call is safe to call
+ *     from several host threads on different streams.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns; results are ready when
  *     the stream is.
@@ -131,6 +132,33 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len,
                      int sp, int B, int N, int Hl, int d, int causal, int dtype, void* stream);
+
+/*
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * computation, arguments and results as ulysses_attn_bwd, without the
+ * workspace: its contents (-D and lse in log2 units, two floats per (rank,
+ * batch row, head, token)) go to a scratch array of ULY_NOALLOC_SCRATCH_BYTES
+ * that the library holds in device memory, one per GPU, from the first call
+ * on that GPU until the process ends. The call allocates nothing.
+ *   - The scratch of the calling thread's current device is used: make it the
+ *     device of the stream and the tensors.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents (nothing in it needs to start at zero). Calls that
+ *     overlap in time on one GPU (on different streams, or from different
+ *     host threads) race and give wrong results: serialise them on one
+ *     stream, or give each its own workspace through ulysses_attn_bwd.
+ *   - Limit: ulysses_attn_bwd_workspace_bytes(...) <= ULY_NOALLOC_SCRATCH_BYTES,
+ *     i.e. sp * B * Hl * N <= 8388608 (token, head) rows.
+ * Errors: as ulysses_attn_bwd; ULY_EWORKSPACE when the problem needs more
+ * scratch than the limit; ULY_EHIP when the scratch's device address cannot
+ * be looked up.
+ */
+#define ULY_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                             const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int ndoc,
+                             int max_doc_len, int sp, int B, int N, int Hl, int d, int causal, int dtype,
+                             void* stream);
 
 /*
  * Ring attention, the other sequence-parallel mode (ColossalAI docs,

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) == {
         "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
-        "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string",
+        "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_attn_bwd_noalloc",
         "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
         "ulysses_ring_attn_bwd_step", "ulysses_sp_loss_workspace_bytes", "ulysses_sp_loss",
     }
@@ -87,6 +87,28 @@ def test_attention_argument_errors():
     assert bwd(*ptrs, None, need, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
     assert bwd(*ptrs[:8], None, FAKE, need, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
     assert bwd(*ptrs, FAKE, need, None, 1, 8, 1, 1, 8, 2, 64, 1, 9, None) == EUNSUP
+
+
+def test_noalloc_argument_errors():
+    """Refusals happen on the host, before the scratch's address is looked up."""
+    lib = uly.library()
+    f = lib.ulysses_attn_bwd_noalloc
+    ptrs = [FAKE] * 9
+    assert f(*ptrs[:8], None, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
+    assert f(*ptrs, None, 1, 8, 1, 1, 8, 2, 48, 1, 1, None) == EUNSUP
+    assert f(*ptrs, FAKE, 1, 9, 1, 1, 8, 2, 64, 1, 1, None) == ESHAPE  # max_doc_len > N
+    # sp * B * Hl * N = 8388609 rows: one more than the scratch holds
+    assert f(*ptrs, None, 1, 1, 1, 1, 8388609, 1, 64, 1, 1, None) == EWS
+    assert f(*ptrs, None, 1, 1, 4, 2, 1048577, 1, 64, 1, 1, None) == EWS
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define ULY_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m, "ULY_NOALLOC_SCRATCH_BYTES not found in the header"
+    assert int(m.group(1)) << int(m.group(2)) == uly.ULY_NOALLOC_SCRATCH_BYTES
+    # the limit in rows stated in the header: two floats per (token, head) row
+    assert uly.ULY_NOALLOC_SCRATCH_BYTES // 8 == 8388608
 
 
 def test_workspace_is_linear_in_n():

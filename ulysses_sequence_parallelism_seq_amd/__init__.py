@@ -13,6 +13,9 @@ Functions carry the C names:
   ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)
   ulysses_attn_bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)
   ulysses_attn_bwd_workspace_bytes(...), ulysses_status_string(code)
+  ulysses_attn_bwd_noalloc(q, k, v, o, dout, lse, ..., dq=, dk=, dv=)
+                                          the backward without a workspace (the
+                                          library's fixed per-GPU scratch)
   ulysses_ring_attn_fwd_step(q, k, v, step, ...) one ring step (running o_acc, lse)
   ulysses_ring_attn_bwd_prepare(o, dout, lse)     D and lse*log2(e) into a workspace
   ulysses_ring_attn_bwd_step(q, k, v, dout, lse, workspace, step, ...)
@@ -60,6 +63,7 @@ def library() -> ctypes.CDLL:
         lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.ulysses_attn_bwd_workspace_bytes.restype = sz
         lib.ulysses_attn_bwd.argtypes = [vp] * 10 + [sz, vp] + [i] * 9 + [vp]
+        lib.ulysses_attn_bwd_noalloc.argtypes = [vp] * 10 + [i] * 9 + [vp]
         lib.ulysses_ring_attn_fwd_step.argtypes = [vp] * 6 + [i] * 8 + [vp]
         lib.ulysses_ring_attn_bwd_workspace_bytes.argtypes = [i] * 6
         lib.ulysses_ring_attn_bwd_workspace_bytes.restype = sz
@@ -71,6 +75,7 @@ def library() -> ctypes.CDLL:
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
         for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
+                     "ulysses_attn_bwd_noalloc",
                      "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
                      "ulysses_sp_loss"):
             getattr(lib, name).restype = i
@@ -226,6 +231,37 @@ def ulysses_attn_bwd(q, k, v, o, dout, lse, cu_seqlens=None, causal: bool = True
     return dq, dk, dv
 
 
+# The fixed per-GPU scratch of ulysses_attn_bwd_noalloc (ULY_NOALLOC_SCRATCH_BYTES in ulysses.h).
+ULY_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def ulysses_attn_bwd_noalloc(q, k, v, o, dout, lse, cu_seqlens=None, causal: bool = True, dq=None, dk=None,
+                             dv=None):
+    """Attention backward without a workspace; returns (dq, dk, dv).
+
+    The library's own scratch replaces the workspace, so a caller that passes
+    dq, dk, dv and a DocPacking (or None) makes the call allocate nothing.
+    Calls that overlap on one GPU share that scratch and race.
+    """
+    sp, B, N, Hl, d = _share_shape(q)
+    for t in (k, v, o, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, o, dout must share shape and dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _expect(lse, tuple(q.shape[:-3]) + (Hl, N), torch.float32, "lse")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, q.shape, q.dtype, name)
+    _require_device(q, k, v, o, dout, lse, dq, dk, dv)
+    cu_dev, ndoc, maxlen = _packing(cu_seqlens, N, q.device)
+    with torch.cuda.device(q.device):  # the scratch used is the current device's
+        _check("ulysses_attn_bwd_noalloc", library().ulysses_attn_bwd_noalloc(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            _ptr(cu_dev), ndoc, maxlen, sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
+    return dq, dk, dv
+
+
 # ---------------------------------------------------------------- ring attention
 # q, k, v, dout, o: [sp, B, Ns, H, d] bf16 chunks (rank r holds tokens r*Ns ..);
 # lse: [sp, B, H, Ns] float32.
@@ -367,6 +403,8 @@ __all__ = [
     "ulysses_attn_fwd",
     "ulysses_attn_bwd",
     "ulysses_attn_bwd_workspace_bytes",
+    "ulysses_attn_bwd_noalloc",
+    "ULY_NOALLOC_SCRATCH_BYTES",
     "ulysses_status_string",
     "ulysses_ring_attn_fwd_step",
     "ulysses_ring_attn_bwd_prepare",

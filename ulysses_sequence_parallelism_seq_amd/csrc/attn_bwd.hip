@@ -33,6 +33,8 @@
 
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -899,4 +901,52 @@ extern "C" int ulysses_attn_bwd(const void* q, const void* k, const void* v, con
         static_cast<const float*>(o), static_cast<const float*>(dout), lse, static_cast<float*>(dq),
         static_cast<float*>(dk), static_cast<float*>(dv), delta, g, stream);
   return uly_host::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, g, stream);
+}
+
+// ----------------------------------------------------- no-allocation variant
+// ulysses_attn_bwd_noalloc keeps what the workspace of ulysses_attn_bwd holds
+// (-D and lse in log2 units, two floats per row) in this file-scope array
+// instead: one copy on every GPU the library runs on, from the module's load
+// until the process ends. In host code `scratch` names a host-side stand-in,
+// not device memory, so the kernels are given the device address looked up
+// once per device with hipGetSymbolAddress.
+static_assert(ULY_NOALLOC_SCRATCH_BYTES % 256 == 0, "whole 256-byte blocks");
+static __device__ __align__(256) float scratch[ULY_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[kMaxDevices];  // device address of `scratch` on device i, once looked up
+
+// The scratch address on the calling thread's current device.
+int current_device_scratch(float** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return ULY_EHIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return ULY_EHIP;
+    g_scratch_dev[dev] = static_cast<float*>(p);
+  }
+  *out = g_scratch_dev[dev];
+  return ULY_OK;
+}
+
+}  // namespace
+
+extern "C" int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                                        const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B,
+                                        int N, int Hl, int d, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ULY_EINVAL;
+  const int rc = uly_host::check_attn_args(ndoc, max_doc_len, cu_seqlens, sp, B, N, Hl, d, dtype);
+  if (rc != ULY_OK) return rc;
+  const size_t need = ulysses_attn_bwd_workspace_bytes(sp, B, N, Hl, d, dtype);
+  if (need > ULY_NOALLOC_SCRATCH_BYTES) return ULY_EWORKSPACE;
+  float* ws = nullptr;
+  const int src = current_device_scratch(&ws);
+  if (src != ULY_OK) return src;
+  return ulysses_attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, ws, need, cu_seqlens, ndoc, max_doc_len, sp, B,
+                          N, Hl, d, causal, dtype, stream);
 }
