@@ -16,6 +16,9 @@ Contents:
              partial results merged by their log-sum-exp; its backward.
   loss       the sequence-parallel loss aggregation: per-rank mean loss and
              counted-token count, combined as a count-weighted mean.
+  mlp        ALST's tiled MLP: the SwiGLU FFN over a rank's tokens, whole or
+             tile by tile (intermediates recomputed in the backward, weight
+             gradients accumulated over the tiles).
 
 Every function here is pinned by tests that do not call it twice: closed
 forms, finite differences, brute-force loops, an independent library
@@ -32,4 +35,5 @@ from .attention import (  # noqa: F401
     doc_ids,
 )
 from .loss import sp_loss, rank_losses, aggregate  # noqa: F401
+from .mlp import mlp_fwd, mlp_bwd, tiled_mlp_fwd, tiled_mlp_bwd, mlp_bwd_weight_units  # noqa: F401
 from .ring import ring_fwd, ring_bwd, ring_chunk, block_mode, block_attn, merge, stitch, stitch_lse  # noqa: F401
