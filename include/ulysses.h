@@ -255,6 +255,41 @@ int ulysses_sp_loss(const float* token_loss, const long long* labels, float* ran
                     long long* good_tokens, float* loss, void* workspace, size_t workspace_bytes,
                     int sp, int B, int Ns, int ignore_index, void* stream);
 
+/*
+ * Tiled MLP of ALST (HF guide "Ulysses sequence parallelism", the paragraph
+ * after the layout diagram: Arctic Long Sequence Training pairs Ulysses with
+ * TiledMLP; jianying88 guide, its account of the layout: after the second
+ * all-to-all the FFN runs locally on each rank's token shard). The FFN is the
+ * Llama-style SwiGLU MLP of one rank's tokens,
+ *   G = X Wg^T,  U = X Wu^T,  A = silu(G) * U,  Y = A Wd^T,  silu(z) = z / (1 + e^-z),
+ * computed over tiles of `tile` tokens so that only one tile's [tile, inter]
+ * intermediates exist (in the workspace) at a time; the backward recomputes
+ * them per tile and accumulates the weight gradients over the tiles:
+ *   dA = dY Wd,  dWd = sum dY^T A,  dG = dA * U * silu'(G),  dU = dA * silu(G),
+ *   dX = dG Wg + dU Wu,  dWg = sum dG^T X,  dWu = sum dU^T X.
+ * The result equals the MLP over all tokens at once (up to rounding).
+ *   x, dy, y, dx   [tokens][hidden] bf16 (y, dx fully overwritten)
+ *   w_gate, w_up   [inter][hidden] bf16;  w_down [hidden][inter] bf16
+ *   dw_gate, dw_up [inter][hidden] float; dw_down [hidden][inter] float:
+ *                  fully overwritten with the sums over every token
+ *   workspace      >= ulysses_tiled_mlp_workspace_bytes(...) bytes: three
+ *                  [tile][inter] bf16 arrays of one tile (A, and the backward's
+ *                  U * silu'(G) and silu(G)); contents on entry ignored
+ * bf16 only. hidden and inter must be multiples of 256 (Llama-7B: 4096 and
+ * 11008); tokens and tile are any positive sizes (the last tile may be short).
+ * Pointers must be 16-byte aligned.
+ * Errors: ULY_EINVAL (null pointer, size <= 0), ULY_ESHAPE (hidden or inter
+ * not a multiple of 256, or 512 * max(hidden, inter) >= 2^31),
+ * ULY_EWORKSPACE, ULY_EHIP.
+ */
+size_t ulysses_tiled_mlp_workspace_bytes(int tokens, int hidden, int inter, int tile);
+int ulysses_tiled_mlp_fwd(const void* x, const void* w_gate, const void* w_up, const void* w_down, void* y,
+                          void* workspace, size_t workspace_bytes, int tokens, int hidden, int inter, int tile,
+                          void* stream);
+int ulysses_tiled_mlp_bwd(const void* x, const void* w_gate, const void* w_up, const void* w_down, const void* dy,
+                          void* dx, float* dw_gate, float* dw_up, float* dw_down, void* workspace,
+                          size_t workspace_bytes, int tokens, int hidden, int inter, int tile, void* stream);
+
 /* Static English text for a status code (never NULL). */
 const char* ulysses_status_string(int status);
 

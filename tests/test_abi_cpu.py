@@ -32,6 +32,7 @@ def test_library_exports_every_declared_function():
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_attn_bwd_noalloc",
         "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
         "ulysses_ring_attn_bwd_step", "ulysses_sp_loss_workspace_bytes", "ulysses_sp_loss",
+        "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
     }
     for n in names:
         assert hasattr(lib, n), n
@@ -186,3 +187,24 @@ def test_ring_binding_needs_running_state_after_step_0():
         uly.ulysses_ring_attn_fwd_step(q, q, q, 1, True)
     with pytest.raises(ValueError):
         uly.ulysses_ring_attn_bwd_step(q, q, q, q, torch.zeros(2, 1, 2, 8), torch.zeros(8, dtype=torch.uint8), 1)
+
+
+def test_tiled_mlp_argument_errors():
+    lib = uly.library()
+    ws = lib.ulysses_tiled_mlp_workspace_bytes
+    assert ws(16384, 4096, 11008, 4096) == 3 * 4096 * 11008 * 2  # three [tile][inter] bf16 arrays of one tile
+    assert ws(100, 256, 512, 4096) == 3 * 100 * 512 * 2  # a tile larger than the tokens holds only them
+    assert ws(100, 100, 512, 64) == 0 and ws(0, 256, 256, 64) == 0 and ws(8, 256, 256, 0) == 0
+    need = ws(300, 256, 512, 128)
+    fwd = lib.ulysses_tiled_mlp_fwd
+    assert fwd(None, FAKE, FAKE, FAKE, FAKE, FAKE, need, 300, 256, 512, 128, None) == EINVAL
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 300, 250, 512, 128, None) == ESHAPE  # hidden % 256
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 300, 256, 500, 128, None) == ESHAPE  # inter % 256
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 300, 256, 512, 0, None) == EINVAL
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, 300, 256, 512, 128, None) == EWS
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, need, 300, 256, 512, 128, None) == EWS
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need, 300, 1 << 22, 512, 128, None) == ESHAPE  # 2 GiB tiles
+    bwd = lib.ulysses_tiled_mlp_bwd
+    assert bwd(*([FAKE] * 8), None, FAKE, need, 300, 256, 512, 128, None) == EINVAL  # dw_down
+    assert bwd(*([FAKE] * 9), FAKE, need - 1, 300, 256, 512, 128, None) == EWS
+    assert bwd(*([FAKE] * 9), FAKE, need, -1, 256, 512, 128, None) == EINVAL

@@ -26,3 +26,4 @@ def test_frag_offsets_match_tile_layout(tmp_path):
     r = subprocess.run([str(exe)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "mismatches d=64: 0 d=128: 0" in r.stdout
+    assert "natural-order transposing reads, mismatches d=64: 0 d=128: 0" in r.stdout

@@ -22,6 +22,9 @@ Functions carry the C names:
   ulysses_ring_attn_bwd_workspace_bytes(...)
 and two loops over the ring steps, ring_attn_fwd and ring_attn_bwd.
   ulysses_sp_loss(token_loss, labels)      -> (loss, rank_loss, good_tokens)
+  ulysses_tiled_mlp_fwd(x, wg, wu, wd, tile) -> y           ALST's tiled SwiGLU MLP
+  ulysses_tiled_mlp_bwd(x, wg, wu, wd, dy, tile) -> (dx, dwg, dwu, dwd)
+  ulysses_tiled_mlp_workspace_bytes(tokens, hidden, inter, tile)
 """
 
 from __future__ import annotations
@@ -72,12 +75,16 @@ def library() -> ctypes.CDLL:
         lib.ulysses_sp_loss_workspace_bytes.argtypes = [i, i, i]
         lib.ulysses_sp_loss_workspace_bytes.restype = sz
         lib.ulysses_sp_loss.argtypes = [vp] * 6 + [sz] + [i] * 4 + [vp]
+        lib.ulysses_tiled_mlp_workspace_bytes.argtypes = [i] * 4
+        lib.ulysses_tiled_mlp_workspace_bytes.restype = sz
+        lib.ulysses_tiled_mlp_fwd.argtypes = [vp] * 6 + [sz] + [i] * 4 + [vp]
+        lib.ulysses_tiled_mlp_bwd.argtypes = [vp] * 10 + [sz] + [i] * 4 + [vp]
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
         for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
                      "ulysses_attn_bwd_noalloc",
                      "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
-                     "ulysses_sp_loss"):
+                     "ulysses_sp_loss", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd"):
             getattr(lib, name).restype = i
         _lib = lib
     return _lib
@@ -394,6 +401,68 @@ def ulysses_sp_loss(token_loss, labels, ignore_index: int = -100, workspace=None
     return loss, rank_loss, good_tokens
 
 
+# ------------------------------------------------------------------ tiled MLP
+# x, y, dy, dx: [tokens, hidden] bf16; wg, wu: [inter, hidden] bf16; wd: [hidden, inter] bf16;
+# weight gradients fp32, same shapes as the weights.
+
+
+def ulysses_tiled_mlp_workspace_bytes(tokens: int, hidden: int, inter: int, tile: int) -> int:
+    return int(library().ulysses_tiled_mlp_workspace_bytes(tokens, hidden, inter, tile))
+
+
+def _mlp_shapes(x, wg, wu, wd):
+    if x.dim() != 2 or x.dtype != torch.bfloat16:
+        raise ValueError("x must be [tokens, hidden] bfloat16")
+    tokens, hidden = x.shape
+    inter = wg.shape[0]
+    _expect(wg, (inter, hidden), torch.bfloat16, "w_gate")
+    _expect(wu, (inter, hidden), torch.bfloat16, "w_up")
+    _expect(wd, (hidden, inter), torch.bfloat16, "w_down")
+    return tokens, hidden, inter
+
+
+def _mlp_workspace(tokens, hidden, inter, tile, workspace, device):
+    need = ulysses_tiled_mlp_workspace_bytes(tokens, hidden, inter, tile)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    return workspace
+
+
+def ulysses_tiled_mlp_fwd(x, w_gate, w_up, w_down, tile: int, workspace=None, y=None):
+    """Y = (silu(x Wg^T) * (x Wu^T)) Wd^T over tiles of `tile` tokens; returns y."""
+    tokens, hidden, inter = _mlp_shapes(x, w_gate, w_up, w_down)
+    workspace = _mlp_workspace(tokens, hidden, inter, tile, workspace, x.device)
+    y = torch.empty_like(x) if y is None else y
+    _expect(y, x.shape, x.dtype, "y")
+    _require_device(x, w_gate, w_up, w_down, y, workspace)
+    _check("ulysses_tiled_mlp_fwd", library().ulysses_tiled_mlp_fwd(
+        _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(y), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), tokens, hidden, inter, int(tile), _stream(x)))
+    return y
+
+
+def ulysses_tiled_mlp_bwd(x, w_gate, w_up, w_down, dy, tile: int, workspace=None, dx=None, dw_gate=None,
+                          dw_up=None, dw_down=None):
+    """Gradients of the tiled MLP; returns (dx, dw_gate, dw_up, dw_down), weight gradients in fp32."""
+    tokens, hidden, inter = _mlp_shapes(x, w_gate, w_up, w_down)
+    _expect(dy, x.shape, x.dtype, "dy")
+    workspace = _mlp_workspace(tokens, hidden, inter, tile, workspace, x.device)
+    f32 = lambda t: torch.empty(t.shape, dtype=torch.float32, device=x.device)  # noqa: E731
+    dx = torch.empty_like(x) if dx is None else dx
+    dw_gate = f32(w_gate) if dw_gate is None else dw_gate
+    dw_up = f32(w_up) if dw_up is None else dw_up
+    dw_down = f32(w_down) if dw_down is None else dw_down
+    _expect(dx, x.shape, x.dtype, "dx")
+    for name, t, wt in (("dw_gate", dw_gate, w_gate), ("dw_up", dw_up, w_up), ("dw_down", dw_down, w_down)):
+        _expect(t, wt.shape, torch.float32, name)
+    _require_device(x, w_gate, w_up, w_down, dy, dx, dw_gate, dw_up, dw_down, workspace)
+    _check("ulysses_tiled_mlp_bwd", library().ulysses_tiled_mlp_bwd(
+        _ptr(x), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dy), _ptr(dx), _ptr(dw_gate), _ptr(dw_up),
+        _ptr(dw_down), _ptr(workspace), workspace.numel() * workspace.element_size(), tokens, hidden, inter,
+        int(tile), _stream(x)))
+    return dx, dw_gate, dw_up, dw_down
+
+
 __all__ = [
     "DocPacking",
     "UlyssesError",
@@ -413,4 +482,7 @@ __all__ = [
     "ring_attn_fwd",
     "ring_attn_bwd",
     "ulysses_sp_loss",
+    "ulysses_tiled_mlp_workspace_bytes",
+    "ulysses_tiled_mlp_fwd",
+    "ulysses_tiled_mlp_bwd",
 ]

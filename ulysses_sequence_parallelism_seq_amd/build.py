@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libulysses.so")
-SOURCES = ["permute.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip", "ring.hip", "sp_loss.hip"]
+SOURCES = ["permute.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_f32.hip", "ring.hip", "sp_loss.hip", "mlp.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

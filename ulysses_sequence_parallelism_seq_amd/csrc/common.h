@@ -219,6 +219,35 @@ __device__ __forceinline__ bf16x8 a_from_rows_at(const bf16* tile, const FragOff
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
+// The same transposing reads addressed for the natural k order: lane l
+// (h = l / 32) receives column c0 + l % 32 of rows t0 + 8h + (0..3) (first
+// read) and t0 + 8h + 4 + (0..3) (second), so MFMA k index 8h + i is row
+// t0 + 8h + i, the order a 16-byte read of a K-contiguous operand gives.
+// GEMMs that pair such an operand with a K-strided one read both in this order.
+template <int D>
+struct NatTrOffsets {
+  uint32_t lo, hi;
+  __host__ __device__ __forceinline__ void init(int lane) {
+    const int half = lane >> 5, p = lane & 15;
+    const int r0 = 8 * half + (p >> 2);
+    const int cl = 2 * ((lane >> 4) & 1) + ((p & 3) >> 1);
+    const uint32_t low = (uint32_t)(4 * (p & 1)) * 2u;
+    lo = (uint32_t)(r0 * 2 * D) + ((uint32_t)(cl ^ RowTile<D>::chunk_key(r0)) << 4) + low;
+    hi = (uint32_t)((r0 + 4) * 2 * D) + ((uint32_t)(cl ^ RowTile<D>::chunk_key(r0 + 4)) << 4) + low;
+  }
+};
+
+// MFMA operand (rows = columns c0 .. c0+31 of a [k][D] RowTile<D> LDS tile,
+// k = rows t0 .. t0+15 in the natural order), t0 = 16 j, c0 = 32 cb.
+template <int D>
+__device__ __forceinline__ bf16x8 a_from_rows_nat(const bf16* tile, const NatTrOffsets<D>& no, int j, int cb) {
+  const char* t = reinterpret_cast<const char*>(tile) + j * 32 * D;
+  const uint32_t x = (uint32_t)cb << 6;
+  const uint2 lo = lds_read_tr16(reinterpret_cast<const bf16*>(t + (no.lo ^ x)));
+  const uint2 hi = lds_read_tr16(reinterpret_cast<const bf16*>(t + (no.hi ^ x)));
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
 // Value held by lane (l ^ 32) of the wave.
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32, 64); }
 

@@ -145,3 +145,23 @@ def random_bits(shape, seed: int, dtype: str) -> torch.Tensor:
         return raw.view(torch.bfloat16)
     raw = torch.randint(-(1 << 31), (1 << 31) - 1, shape, generator=g, dtype=torch.int32)
     return raw.view(torch.float32)
+
+
+# ------------------------------------------------------------- tiled MLP inputs
+# The FFN of the Llama-style model the workloads are shaped like: hidden =
+# H * d = 4096 and the Llama-7B intermediate width 11008; its tokens are one
+# rank's sequence shard (N / sp of them). Weights are drawn like a standard
+# initialisation, N(0, 1/fan_in), activations and their gradients N(0, 1).
+MLP_HIDDEN, MLP_INTER = 4096, 11008
+
+
+def mlp_inputs(tokens: int, hidden: int, inter: int, seed: int, dtype: str = "bf16"):
+    """x [tokens, hidden], w_gate, w_up [inter, hidden], w_down [hidden, inter],
+    dy [tokens, hidden], drawn in that order from one seeded CPU generator."""
+    g = torch.Generator().manual_seed(seed)
+    x = randn((tokens, hidden), g, dtype)
+    wg = randn((inter, hidden), g, dtype, hidden ** -0.5)
+    wu = randn((inter, hidden), g, dtype, hidden ** -0.5)
+    wd = randn((hidden, inter), g, dtype, inter ** -0.5)
+    dy = randn((tokens, hidden), g, dtype)
+    return x, wg, wu, wd, dy
