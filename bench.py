@@ -6,7 +6,7 @@ workload, B=1, N=131072, H=32, sp=8, d=128, bf16, causal):
   seq_to_head(q), (k), (v)          8 shards [16384, 32, 128] -> 8 shares [131072, 4, 128]
   attn_fwd over the 8 shares         saves lse only
   head_to_seq(o), seq_to_head(dO)
-  attn_bwd over the 8 shares         D pre-pass + dK/dV + dQ kernels
+  attn_bwd over the 8 shares         D pre-pass, then dK/dV + dQ kernels (two calls)
   head_to_seq(dq), (dk), (dv)
 Inputs are seeded synthetic tensors already resident in HBM. Every call is
 timed with HIP events on the stream it runs on.
@@ -24,6 +24,14 @@ change; sp forward ring steps (each rank's queries against the key/value
 chunk passed to it, partial results merged by log-sum-exp), the D pre-pass,
 then sp backward ring steps. Same FLOP count, same value definition.
 
+With --variant tiledmlp it times ALST's tiled MLP instead: the Llama-7B
+SwiGLU FFN (hidden 4096, inter 11008) over every virtual rank's token shard
+of the workload (sp x B x N/sp tokens, one call with the shared weights, the
+same work as sp rank calls plus the sum of their weight gradients), in tiles
+of --mlp-tile tokens: forward and backward per step. value = FLOPs counted as
+22 * hidden * inter per token (forward 6, backward 12, plus the forward's
+gate and up products recomputed per tile, 4) per second.
+
 With --variant loss it times the sequence-parallel loss aggregation on the
 workload's tokens instead (sp ranks x B rows x N/sp tokens: per-token fp32
 losses and int64 labels, 30% of them -100): value = bytes read (12 per
@@ -38,6 +46,7 @@ import argparse
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -94,7 +103,7 @@ def make_buffers(w: workloads.Workload, dev):
 
 
 class Timer:
-    """HIP-event timing of each named call over the timed steps."""
+    """HIP-event timing of each named call over the timed steps (per-call median)."""
 
     def __init__(self, stream):
         self.stream = stream
@@ -110,10 +119,11 @@ class Timer:
         return out
 
     def averages(self):
+        """Median duration (ms) of each named call, and how many were timed."""
         acc = {}
         for name, a, b in self.pending:
             acc.setdefault(name, []).append(a.elapsed_time(b))
-        return {k: statistics.mean(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
+        return {k: statistics.median(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
 def step(w, bufs, packing, timer=None):
@@ -129,8 +139,10 @@ def step(w, bufs, packing, timer=None):
     run("attn_fwd", lambda: uly.ulysses_attn_fwd(qh, kh, vh, packing, w.causal, out=o, lse=lse))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(o, out=os_))
     run("seq_to_head", lambda: uly.ulysses_seq_to_head(dos, out=doh))
-    run("attn_bwd", lambda: uly.ulysses_attn_bwd(qh, kh, vh, o, doh, lse, packing, w.causal, workspace=ws,
-                                                 dq=dq, dk=dk, dv=dv))
+    # ulysses_attn_bwd in its two steps, timed apart: the D pre-pass, then the dK/dV and dQ kernels
+    run("attn_bwd_prepare", lambda: uly.ulysses_attn_bwd_prepare(o, doh, lse, ws))
+    run("attn_bwd_prepared", lambda: uly.ulysses_attn_bwd_prepared(qh, kh, vh, doh, lse, ws, packing, w.causal,
+                                                                   dq=dq, dk=dk, dv=dv))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dq, out=dqs))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dk, out=dks))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dv, out=dvs))
@@ -168,8 +180,26 @@ def ring_step(w, bufs, timer=None):
                                                                      dqa, dka, dva, dq, dk, dv))
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name, from lscpu (else /proc/cpuinfo)."""
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except (OSError, subprocess.SubprocessError):
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        return "unknown"
+
+
 def cpu_baseline(w: workloads.Workload, target_s: float):
-    """The float64 oracle, fwd + bwd, on the causal prefix of one head (bounded sample)."""
+    """The float64 oracle, fwd + bwd, timed on a causal prefix of one head (a
+    bounded sample of about target_s seconds), and the time of the whole
+    configuration extrapolated from it by the exact ratio of causal pairs."""
     import oracle
 
     try:
@@ -197,21 +227,26 @@ def cpu_baseline(w: workloads.Workload, target_s: float):
     M2 = max(2048, min(int(M * (target_s / max(t, 1e-3)) ** 0.5) // 256 * 256, w.N))
     if M2 > M:
         M, t = M2, run(M2)
-    flops = 14 * w.d * (M * (M + 1) // 2)
-    cpu_model = "unknown"
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((line.split(":", 1)[1].strip() for line in f if line.startswith("model name")), cpu_model)
-    except OSError:
-        pass
+    pairs_sample = M * (M + 1) // 2
+    flops = 14 * w.d * pairs_sample
+    pairs_head = causal_pairs(w)
+    pairs_config = pairs_head * w.sp * w.B * w.Hl
     return {
         "value": flops / t / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
-        "cpu_model": cpu_model,
+        "cpu_model": _cpu_model(),
+        "openblas_num_threads": os.environ.get("OPENBLAS_NUM_THREADS", "unset"),
+        "omp_num_threads": os.environ.get("OMP_NUM_THREADS", "unset"),
         "kind": "oracle",
         "sample": f"float64 oracle fwd+bwd of one head, causal prefix of {M} of the {w.N} tokens "
                   f"({t:.1f} s; FLOPs counted as 14*d*pairs like the GPU value)",
+        "sample_s": round(t, 2),
+        "extrapolated_one_head_s": round(t * pairs_head / pairs_sample, 1),
+        "extrapolated_config_s": round(t * pairs_config / pairs_sample, 1),
+        "extrapolation": f"extrapolated by the exact causal pair ratio: one head {pairs_head} pairs, the whole "
+                         f"configuration ({w.sp * w.B * w.Hl} rank x row x head units) {pairs_config} pairs, "
+                         f"against {pairs_sample} in the sample",
     }
 
 
@@ -223,7 +258,8 @@ def main():
     ap.add_argument("--workload", default="long", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--variant", default="ulysses", choices=["ulysses", "ring", "loss"])
+    ap.add_argument("--variant", default="ulysses", choices=["ulysses", "ring", "loss", "tiledmlp"])
+    ap.add_argument("--mlp-tile", type=int, default=4096)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -238,6 +274,8 @@ def main():
     cu = workloads.workload_cu_seqlens(w)
     if args.variant == "loss":
         return loss_main(args, w, dev)
+    if args.variant == "tiledmlp":
+        return mlp_main(args, w, dev)
     if args.variant == "ring":
         if cu is not None or w.dtype != "bf16":
             print("the ring variant runs bf16 workloads with one document per row", file=sys.stderr)
@@ -261,6 +299,8 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     avg, counts = timer.averages()
+    # the backward = its D pre-pass + the dK/dV and dQ kernels, each timed on its own
+    avg["attn_bwd"] = avg["attn_bwd_prepare"] + avg["attn_bwd_prepared"]
 
     # reference for the permute: a plain device-to-device copy of one tensor of the same size
     copy_dst = torch.empty_like(seq_in[0])
@@ -304,6 +344,12 @@ def main():
             "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
             "attn_fwd_ms": round(avg["attn_fwd"], 3),
             "attn_bwd_ms": round(avg["attn_bwd"], 3),
+            "attn_bwd_prepare_ms": round(avg["attn_bwd_prepare"], 4),
+            "attn_bwd_prepared_ms": round(avg["attn_bwd_prepared"], 3),
+            # the D pre-pass reads O and dO (2 d esize per row) and lse, writes -D and lse2 (8 bytes)
+            "attn_bwd_prepare_gbs": round(w.sp * w.B * w.Hl * w.N * (2 * w.d * esize + 12)
+                                          / (avg["attn_bwd_prepare"] * 1e-3) / 1e9, 1),
+            "timing": f"HIP events on the launch stream, per-call medians over {args.steps} steps",
             "attn_fwd_tflops": round(fwd_tflops, 1),
             "attn_bwd_tflops": round(bwd_tflops, 1),
             "attn_only_tflops": round(flops_step / (attn_ms * 1e-3) / 1e12, 1),
@@ -311,6 +357,14 @@ def main():
             "permute_gbs": round(permute_gbs, 1),
             "permute_pct_of_hbm_peak": round(100 * permute_gbs / PEAK_HBM_GBS, 1),
             "d2d_copy_gbs": round(2 * tensor_bytes / (copy_ms * 1e-3) / 1e9, 1),
+            # HBM bytes of one permute call from the rocprofv3 counters (calibrated on a plain
+            # device copy), against the algorithmic read + write of every element
+            "permute_counter_bytes": None if traffic is None else {
+                k: round(v) for k, v in traffic["permute"].items()},
+            "permute_counter_gbs": None if traffic is None else {
+                k: round(v / (avg["seq_to_head" if k.endswith("head") else "head_to_seq"] * 1e-3) / 1e9, 1)
+                for k, v in traffic["permute"].items()},
+            "permute_algorithmic_bytes": 2 * tensor_bytes,
             "value_12d_no_recompute": round(12 * w.d * pairs / (ms_per_step * 1e-3) / 1e12, 2),
             "flops_per_step": flops_step,
             "calls_timed": counts,
@@ -323,7 +377,8 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": None if traffic is None else round(traffic["bytes"]),
-            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, calibrated on a plain "
+                            "device-to-device copy of known size)",
             "compulsory_bytes": min_bwd_bytes,
             "flops_per_launch": 10 * w.d * pairs,
         },
@@ -399,6 +454,128 @@ def loss_main(args, w, dev):
         result["cpu_baseline"] = {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": 1,
                                   "kind": "oracle", "sample": f"the float64 oracle on the same tokens, {reps} calls"}
     print(json.dumps(result), flush=True)
+
+
+def mlp_main(args, w, dev):
+    h, inter, tile = workloads.MLP_HIDDEN, workloads.MLP_INTER, args.mlp_tile
+    tokens = w.sp * w.B * w.Ns
+    g = torch.Generator(device=dev).manual_seed(w.seed)
+    x = torch.randn((tokens, h), generator=g, device=dev).bfloat16()
+    dy = torch.randn((tokens, h), generator=g, device=dev).bfloat16()
+    wg = (torch.randn((inter, h), generator=g, device=dev) * h ** -0.5).bfloat16()
+    wu = (torch.randn((inter, h), generator=g, device=dev) * h ** -0.5).bfloat16()
+    wd = (torch.randn((h, inter), generator=g, device=dev) * inter ** -0.5).bfloat16()
+    ws = torch.empty(uly.ulysses_tiled_mlp_workspace_bytes(tokens, h, inter, tile), dtype=torch.uint8, device=dev)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dwg = torch.empty((inter, h), device=dev)
+    dwu = torch.empty((inter, h), device=dev)
+    dwd = torch.empty((h, inter), device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def one_step(timer=None):
+        run = timer.run if timer else (lambda name, fn: fn())
+        run("mlp_fwd", lambda: uly.ulysses_tiled_mlp_fwd(x, wg, wu, wd, tile, ws, y))
+        run("mlp_bwd", lambda: uly.ulysses_tiled_mlp_bwd(x, wg, wu, wd, dy, tile, ws, dx, dwg, dwu, dwd))
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    timer = Timer(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one_step(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    avg, counts = timer.averages()
+    ms_per_step = elapsed * 1e3 / args.steps
+    hi = h * inter * tokens
+    flops_step = 22 * hi
+    value = flops_step / (ms_per_step * 1e-3) / 1e12
+    bwd_tflops = 16 * hi / (avg["mlp_bwd"] * 1e-3) / 1e12
+    result = {
+        "metric": "tiled MLP fwd+bwd TFLOP/s per GPU (% bf16 MFMA peak)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0, 1/fan_in) weights, on the device)",
+        "config": {
+            "workload": f"SwiGLU FFN hidden={h} inter={inter} over {w.name}'s token shards: sp={w.sp} x B={w.B} x "
+                        f"{w.Ns} = {tokens} tokens, tiles of {tile} tokens, bf16",
+            "pct_of_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+            "mlp_fwd_ms": round(avg["mlp_fwd"], 3),
+            "mlp_bwd_ms": round(avg["mlp_bwd"], 3),
+            "mlp_fwd_tflops": round(6 * hi / (avg["mlp_fwd"] * 1e-3) / 1e12, 1),
+            "mlp_bwd_tflops": round(bwd_tflops, 1),
+            "value_18hi_no_recompute": round(18 * hi / (ms_per_step * 1e-3) / 1e12, 2),
+            "flops_per_step": flops_step,
+            "calls_timed": counts,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "kernel": "ulysses_tiled_mlp_bwd (per tile: gate/up recompute, dA, dX, dWd, dWg, dWu GEMMs)",
+            "achieved": round(bwd_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "flops_per_launch": 16 * hi,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = mlp_cpu_baseline(h, inter, tokens, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def mlp_cpu_baseline(h, inter, tokens, target_s):
+    """The float64 MLP oracle, fwd + bwd, on a bounded sample of tokens (about
+    target_s seconds), extrapolated to every token by the token ratio (its work
+    is linear in the tokens)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max((i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"),
+                      default=os.cpu_count())
+    except Exception:
+        threads = os.cpu_count()
+    x, wg, wu, wd, dy = workloads.mlp_inputs(64, h, inter, 1)
+
+    def run(T):
+        xs = x.repeat((T + 63) // 64, 1)[:T]
+        dys = dy.repeat((T + 63) // 64, 1)[:T]
+        t0 = time.perf_counter()
+        oracle.mlp_fwd(xs, wg, wu, wd)
+        oracle.mlp_bwd(xs, wg, wu, wd, dys)
+        return time.perf_counter() - t0
+
+    T = 64
+    t = run(T)
+    while t < target_s / 3 and T < tokens:
+        T = min(2 * T, tokens)
+        t = run(T)
+    flops = 18 * h * inter * T  # the whole-shard oracle recomputes nothing
+    return {
+        "value": flops / t / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "cpu_model": _cpu_model(),
+        "openblas_num_threads": os.environ.get("OPENBLAS_NUM_THREADS", "unset"),
+        "kind": "oracle",
+        "sample": f"float64 MLP oracle fwd+bwd of {T} tokens ({t:.1f} s; FLOPs counted as 18*hidden*inter "
+                  f"per token, its own work)",
+        "sample_s": round(t, 2),
+        "extrapolated_config_s": round(t * tokens / T, 1),
+        "extrapolation": f"extrapolated by the token ratio {tokens}/{T}",
+    }
 
 
 def ring_main(args, w, dev):

@@ -49,7 +49,7 @@ extern "C" {
 /* Status codes. */
 #define ULY_OK 0
 #define ULY_EINVAL 1       /* null pointer where one is required, or a size <= 0 */
-#define ULY_ESHAPE 2       /* N % sp != 0, H % sp != 0, or an inconsistent size */
+#define ULY_ESHAPE 2       /* a size condition fails (each call lists its own) */
 #define ULY_EUNSUPPORTED 3 /* dtype not ULY_F32/ULY_BF16, or d not in {64, 128} */
 #define ULY_EWORKSPACE 4   /* workspace pointer NULL or smaller than required */
 #define ULY_EHIP 5         /* the HIP runtime refused a launch */
@@ -67,8 +67,12 @@ extern "C" {
  * N is the full sequence length. Elements are copied as raw bits (bit-exact,
  * NaN payloads and -0 kept). x_seq and x_head must not overlap and must be
  * 16-byte aligned.
- * Errors: ULY_EINVAL (null, size <= 0, overlap, misaligned), ULY_ESHAPE
- * (N % sp, H % sp), ULY_EUNSUPPORTED (dtype, d), ULY_EHIP.
+ * Errors: ULY_EINVAL (null, size <= 0, overlap, misaligned); ULY_ESHAPE when
+ * N % sp != 0, H % sp != 0, sp > 65535, sp * B >= 2^32, or one shard's
+ * output counts 2^32 - 1024 or more 16-byte chunks: (N/sp) * (H/sp) * d *
+ * esize / 16 here, N * (H/sp) * d * esize / 16 for ulysses_head_to_seq
+ * (esize = 4 for ULY_F32, 2 for ULY_BF16); ULY_EUNSUPPORTED (dtype, d);
+ * ULY_EHIP.
  */
 int ulysses_seq_to_head(const void* x_seq, void* x_head, int B, int N, int H, int d, int sp,
                         int dtype, void* stream);
@@ -101,7 +105,14 @@ int ulysses_head_to_seq(const void* x_head, void* x_seq, int B, int N, int H, in
  *   max_doc_len host int >= the longest document (sizes the launch; a
  *               smaller value leaves rows uncomputed).
  * Errors: ULY_EINVAL (null pointer, size <= 0, ndoc < 1 or max_doc_len < 1
- * with cu_seqlens), ULY_ESHAPE (max_doc_len > N), ULY_EUNSUPPORTED, ULY_EHIP.
+ * with cu_seqlens); ULY_ESHAPE when
+ *   - max_doc_len > N (with cu_seqlens),
+ *   - sp * B * Hl > 2^24 (the (row, head) units of one call),
+ *   - N * Hl * d * esize >= 2^31 (one (row, head) sequence spans 2 GiB or
+ *     more: buffer offsets are 32-bit), or
+ *   - bf16: ceil(L / 256) * ndoc * max(sp * B * Hl, 8) > 2^31 - 1 with L =
+ *     max_doc_len (N without cu_seqlens): the launch's tile index;
+ * ULY_EUNSUPPORTED (dtype, d); ULY_EHIP.
  */
 int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                      const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B, int N,
@@ -126,12 +137,36 @@ size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int
  *                     ulysses_attn_bwd_workspace_bytes(...); contents on
  *                     entry are ignored, on return unspecified.
  * cu_seqlens, ndoc, max_doc_len, causal as in ulysses_attn_fwd.
- * Errors: as ulysses_attn_fwd, plus ULY_EWORKSPACE.
+ * Errors: as ulysses_attn_fwd, with the bf16 tile condition taken with
+ * 128-token tiles, ceil(L / 128) * ndoc * max(sp * B * Hl, 8) > 2^31 - 1;
+ * plus ULY_EWORKSPACE.
  */
 int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len,
                      int sp, int B, int N, int Hl, int d, int causal, int dtype, void* stream);
+
+/*
+ * ulysses_attn_bwd in its two steps, for callers that time or schedule them
+ * apart; ulysses_attn_bwd is exactly ulysses_attn_bwd_prepare followed by
+ * ulysses_attn_bwd_prepared on the same workspace (same kernels, same bits).
+ *   ulysses_attn_bwd_prepare: the D pre-pass alone, from o, dout
+ *     [sp][B][N][Hl][d] and lse [sp][B][Hl][N]: fills the workspace with the
+ *     row sums D_i = sum_c dO_ic O_ic (stored negated for bf16) and, for
+ *     bf16, lse in log2 units. One document per row is assumed for sizing
+ *     only; the values do not depend on the packing.
+ *   ulysses_attn_bwd_prepared: the dK/dV and dQ kernels, reading the
+ *     workspace a prepare call of the same sizes and dtype filled (its
+ *     contents are not checked); q, k, v, dout, lse, dq, dk, dv, cu_seqlens,
+ *     ndoc, max_doc_len, causal as in ulysses_attn_bwd.
+ * Errors: as ulysses_attn_bwd.
+ */
+int ulysses_attn_bwd_prepare(const void* o, const void* dout, const float* lse, void* workspace,
+                             size_t workspace_bytes, int sp, int B, int N, int Hl, int d, int dtype, void* stream);
+int ulysses_attn_bwd_prepared(const void* q, const void* k, const void* v, const void* dout, const float* lse,
+                              void* dq, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                              const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B, int N, int Hl,
+                              int d, int causal, int dtype, void* stream);
 
 /*
  * For callers that cannot allocate device memory: code under HIP graph
@@ -186,8 +221,11 @@ int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const 
  *   o        [sp][B][Ns][H][d] bf16: rank r's rows are written at its last
  *            step (i == r when causal, i == sp-1 otherwise)
  * Steps run in order 0, 1, .., sp-1 (step 0 ignores o_acc and lse on entry).
- * Errors: ULY_EINVAL (null pointer, size <= 0, step outside [0, sp)),
- * ULY_EUNSUPPORTED (dtype, d), ULY_ESHAPE, ULY_EHIP.
+ * Errors: ULY_EINVAL (null pointer, size <= 0, step outside [0, sp));
+ * ULY_EUNSUPPORTED (dtype, d); ULY_ESHAPE when sp * B * H > 2^24,
+ * Ns * H * d * 2 >= 2^31, or ceil(Ns / 128) * max(sp * B * H, 8) > 2^31 - 1
+ * (as for ulysses_attn_bwd, with Ns tokens, H heads, one document);
+ * ULY_EHIP.
  */
 int ulysses_ring_attn_fwd_step(const void* q, const void* k, const void* v, void* o, float* o_acc,
                                float* lse, int step, int sp, int B, int Ns, int H, int d, int causal,
@@ -247,8 +285,8 @@ int ulysses_ring_attn_bwd_step(const void* q, const void* k, const void* v, cons
  *   workspace    >= ulysses_sp_loss_workspace_bytes(sp, B, Ns) bytes, 8-byte
  *                aligned; contents on entry ignored
  * Sums are fp64 in a fixed order (bit-reproducible). sp <= 4096.
- * Errors: ULY_EINVAL (null pointer, size <= 0), ULY_ESHAPE (sp > 4096),
- * ULY_EWORKSPACE, ULY_EHIP.
+ * Errors: ULY_EINVAL (null pointer, size <= 0, B * Ns >= 2^40), ULY_ESHAPE
+ * (sp > 4096), ULY_EWORKSPACE, ULY_EHIP.
  */
 size_t ulysses_sp_loss_workspace_bytes(int sp, int B, int Ns);
 int ulysses_sp_loss(const float* token_loss, const long long* labels, float* rank_loss,

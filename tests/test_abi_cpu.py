@@ -30,6 +30,7 @@ def test_library_exports_every_declared_function():
     assert set(names) == {
         "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_attn_bwd_noalloc",
+        "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
         "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
         "ulysses_ring_attn_bwd_step", "ulysses_sp_loss_workspace_bytes", "ulysses_sp_loss",
         "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
@@ -208,3 +209,42 @@ def test_tiled_mlp_argument_errors():
     assert bwd(*([FAKE] * 8), None, FAKE, need, 300, 256, 512, 128, None) == EINVAL  # dw_down
     assert bwd(*([FAKE] * 9), FAKE, need - 1, 300, 256, 512, 128, None) == EWS
     assert bwd(*([FAKE] * 9), FAKE, need, -1, 256, 512, 128, None) == EINVAL
+
+
+FAR = ctypes.c_void_p(1 << 52)  # a second fake buffer far from FAKE: no overlap at these sizes
+
+
+def test_every_size_limit_in_the_header_is_enforced():
+    """Each ULY_ESHAPE (and size EINVAL) condition ulysses.h lists, triggered on
+    the host before anything is enqueued (fake pointers are never touched)."""
+    lib = uly.library()
+    p2h, h2p = lib.ulysses_seq_to_head, lib.ulysses_head_to_seq
+    assert p2h(FAKE, FAR, 1, 65536 * 2, 65536, 64, 65536, 1, None) == ESHAPE  # sp > 65535
+    assert p2h(FAKE, FAR, 1, 1 << 20, 256, 128, 1, 1, None) == ESHAPE  # seq->head slab: 2^20 * 4096 chunks
+    assert h2p(FAKE, FAR, 1, 1 << 20, 512, 128, 2, 1, None) == ESHAPE  # head->seq slab: 2^20 * 4096 chunks
+    fwd = lib.ulysses_attn_fwd
+
+    def f(cu=None, ndoc=1, maxlen=8, sp=1, B=1, N=8, Hl=2, d=64, dtype=1):
+        return fwd(FAKE, FAKE, FAKE, FAKE, FAKE, cu, ndoc, maxlen, sp, B, N, Hl, d, 1, dtype, None)
+
+    assert f(cu=FAKE, maxlen=9) == ESHAPE  # max_doc_len > N
+    assert f(sp=1, B=1 << 24, Hl=2) == ESHAPE  # sp * B * Hl > 2^24
+    assert f(N=1 << 22, maxlen=1 << 22, Hl=4, d=128) == ESHAPE  # one (row, head) spans 2 GiB
+    assert f(cu=FAKE, ndoc=1 << 20, N=1 << 16, maxlen=1 << 16, B=1 << 11, Hl=2) == ESHAPE  # tile index
+    bwd = lib.ulysses_attn_bwd
+    need = lib.ulysses_attn_bwd_workspace_bytes(1, 1 << 11, 1 << 16, 2, 64, 1)
+    assert need > 0
+    # 128-token backward tiles: ceil(2^16 / 128) * 2^19 * 2^12 > 2^31 - 1 although the forward's
+    # 256-token tiles give exactly 2^31: the backward refuses, the forward does not (its launch
+    # would be huge, so only the refusal is checked here)
+    assert bwd(*([FAKE] * 9), FAKE, need, FAKE, 1 << 19, 1 << 16, 1, 1 << 11, 1 << 16, 2, 64, 1, 1, None) == ESHAPE
+    prep, prepd = lib.ulysses_attn_bwd_prepare, lib.ulysses_attn_bwd_prepared
+    assert prepd(*([FAKE] * 8), FAKE, need, FAKE, 1 << 19, 1 << 16, 1, 1 << 11, 1 << 16, 2, 64, 1, 1, None) == ESHAPE
+    assert prep(FAKE, FAKE, FAKE, FAKE, 7, 1, 1, 8, 2, 64, 1, None) == EWS
+    assert prep(None, FAKE, FAKE, FAKE, 1 << 20, 1, 1, 8, 2, 64, 1, None) == EINVAL
+    assert prepd(*([FAKE] * 8), None, 1 << 20, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    ring = lib.ulysses_ring_attn_fwd_step
+    assert ring(*([FAKE] * 6), 0, 16, 1 << 20, 1 << 20, 1, 64, 1, 1, None) == ESHAPE  # ceil(Ns/256) * units
+    assert ring(*([FAKE] * 6), 0, 2, 1 << 23, 8, 2, 64, 1, 1, None) == ESHAPE  # sp * B * H = 2^25 > 2^24
+    loss = lib.ulysses_sp_loss
+    assert loss(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 2, 1 << 20, 1 << 20, -100, None) == EINVAL  # B*Ns

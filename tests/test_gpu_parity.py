@@ -212,6 +212,24 @@ def test_bf16_packed_equals_separate():
         assert torch.equal(packed[1][..., s:e], alone[1]), "lse"
 
 
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("fp32", 64)])
+def test_backward_in_two_calls_equals_one(dtype, d):
+    """ulysses_attn_bwd_prepare then ulysses_attn_bwd_prepared (the split the
+    benchmark times) give ulysses_attn_bwd's results bit for bit."""
+    say("backward in two calls", dtype, d)
+    dev = device()
+    lengths = [300, 0, 1, 211]
+    packing = uly.DocPacking(workloads.cu_seqlens_from_lengths(lengths), sum(lengths), dev)
+    q, k, v, do = (t.to(dev) for t in workloads.qkv_do((2, 1, sum(lengths), 2, d), 41, dtype))
+    o, lse = uly.ulysses_attn_fwd(q, k, v, packing, True)
+    one = uly.ulysses_attn_bwd(q, k, v, o, do, lse, packing, True)
+    ws = uly.ulysses_attn_bwd_prepare(o, do, lse)
+    two = uly.ulysses_attn_bwd_prepared(q, k, v, do, lse, ws, packing, True)
+    torch.cuda.synchronize()
+    for name, a, b in zip(("dq", "dk", "dv"), one, two):
+        assert torch.equal(a, b), name
+
+
 def test_bf16_bitwise_reproducible():
     say("bf16 reproducible")
     q, k, v, do = workloads.qkv_do((1, 1, 1500, 2, 128), 5, "bf16")

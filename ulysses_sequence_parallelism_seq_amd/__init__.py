@@ -13,6 +13,8 @@ Functions carry the C names:
   ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)
   ulysses_attn_bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)
   ulysses_attn_bwd_workspace_bytes(...), ulysses_status_string(code)
+  ulysses_attn_bwd_prepare(o, dout, lse, workspace)  the D pre-pass alone
+  ulysses_attn_bwd_prepared(q, k, v, dout, lse, workspace, ...)  the rest of the backward
   ulysses_attn_bwd_noalloc(q, k, v, o, dout, lse, ..., dq=, dk=, dv=)
                                           the backward without a workspace (the
                                           library's fixed per-GPU scratch)
@@ -67,6 +69,8 @@ def library() -> ctypes.CDLL:
         lib.ulysses_attn_bwd_workspace_bytes.restype = sz
         lib.ulysses_attn_bwd.argtypes = [vp] * 10 + [sz, vp] + [i] * 9 + [vp]
         lib.ulysses_attn_bwd_noalloc.argtypes = [vp] * 10 + [i] * 9 + [vp]
+        lib.ulysses_attn_bwd_prepare.argtypes = [vp] * 4 + [sz] + [i] * 6 + [vp]
+        lib.ulysses_attn_bwd_prepared.argtypes = [vp] * 9 + [sz, vp] + [i] * 9 + [vp]
         lib.ulysses_ring_attn_fwd_step.argtypes = [vp] * 6 + [i] * 8 + [vp]
         lib.ulysses_ring_attn_bwd_workspace_bytes.argtypes = [i] * 6
         lib.ulysses_ring_attn_bwd_workspace_bytes.restype = sz
@@ -82,7 +86,7 @@ def library() -> ctypes.CDLL:
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
         for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
-                     "ulysses_attn_bwd_noalloc",
+                     "ulysses_attn_bwd_noalloc", "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
                      "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
                      "ulysses_sp_loss", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd"):
             getattr(lib, name).restype = i
@@ -235,6 +239,44 @@ def ulysses_attn_bwd(q, k, v, o, dout, lse, cu_seqlens=None, causal: bool = True
         _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
         _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(cu_dev), ndoc, maxlen,
         sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
+    return dq, dk, dv
+
+
+def ulysses_attn_bwd_prepare(o, dout, lse, workspace=None):
+    """The backward's D pre-pass alone (into the returned workspace)."""
+    sp, B, N, Hl, d = _share_shape(o)
+    if dout.shape != o.shape or dout.dtype != o.dtype:
+        raise ValueError("o and dout must share shape and dtype")
+    need = ulysses_attn_bwd_workspace_bytes(sp, B, N, Hl, d, o.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=o.device)
+    _expect(lse, tuple(o.shape[:-3]) + (Hl, N), torch.float32, "lse")
+    _require_device(o, dout, lse, workspace)
+    _check("ulysses_attn_bwd_prepare", library().ulysses_attn_bwd_prepare(
+        _ptr(o), _ptr(dout), _ptr(lse), _ptr(workspace), workspace.numel() * workspace.element_size(),
+        sp, B, N, Hl, d, _dtype_code(o), _stream(o)))
+    return workspace
+
+
+def ulysses_attn_bwd_prepared(q, k, v, dout, lse, workspace, cu_seqlens=None, causal: bool = True, dq=None,
+                              dk=None, dv=None):
+    """The backward's dK/dV and dQ kernels from a workspace ulysses_attn_bwd_prepare filled."""
+    sp, B, N, Hl, d = _share_shape(q)
+    for t in (k, v, dout):
+        if t.shape != q.shape or t.dtype != q.dtype:
+            raise ValueError("q, k, v, dout must share shape and dtype")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _expect(lse, tuple(q.shape[:-3]) + (Hl, N), torch.float32, "lse")
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _expect(t, q.shape, q.dtype, name)
+    _require_device(q, k, v, dout, lse, workspace, dq, dk, dv)
+    cu_dev, ndoc, maxlen = _packing(cu_seqlens, N, q.device)
+    _check("ulysses_attn_bwd_prepared", library().ulysses_attn_bwd_prepared(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _ptr(cu_dev), ndoc, maxlen, sp, B, N, Hl, d,
+        int(bool(causal)), _dtype_code(q), _stream(q)))
     return dq, dk, dv
 
 
@@ -473,6 +515,8 @@ __all__ = [
     "ulysses_attn_bwd",
     "ulysses_attn_bwd_workspace_bytes",
     "ulysses_attn_bwd_noalloc",
+    "ulysses_attn_bwd_prepare",
+    "ulysses_attn_bwd_prepared",
     "ULY_NOALLOC_SCRATCH_BYTES",
     "ulysses_status_string",
     "ulysses_ring_attn_fwd_step",

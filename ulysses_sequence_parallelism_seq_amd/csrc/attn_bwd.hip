@@ -741,18 +741,29 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
 
 namespace uly_host {
 
-int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
-                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                         float* delta, const AttnGeom& g, void* stream) {
+// The tile decode forms nslots * ndoc * max(units, kUnitGroup) in int, for
+// the dQ kernel's 256-query tiles and the dK/dV kernel's 128-key tiles.
+bool bwd_tiles_fit(const AttnGeom& g) {
+  const long long maxlen = g.cu ? g.max_doc_len : g.N;
+  const long long units = (long long)g.G * g.Hl;
+  const long long ug = units > uly::kUnitGroup ? units : uly::kUnitGroup;
+  return (maxlen + kKvBK - 1) / kKvBK * g.ndoc * ug <= 0x7fffffffLL &&
+         (maxlen + kDqBQ - 1) / kDqBQ * g.ndoc * ug <= 0x7fffffffLL;
+}
+
+int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, const float* delta,
+                              const AttnGeom& g, void* stream) {
+  if (!bwd_tiles_fit(g)) return ULY_ESHAPE;
   BwdArgs a;
   a.q = static_cast<const bf16*>(q);
   a.k = static_cast<const bf16*>(k);
   a.v = static_cast<const bf16*>(v);
-  a.o = static_cast<const bf16*>(o);
+  a.o = nullptr;
   a.dout = static_cast<const bf16*>(dout);
   a.lse = lse;
-  a.delta = delta;
-  a.lse2 = delta + (size_t)g.G * g.Hl * g.N;
+  a.delta = const_cast<float*>(delta);
+  a.lse2 = const_cast<float*>(delta) + (size_t)g.G * g.Hl * g.N;
   a.dq = static_cast<bf16*>(dq);
   a.dk = static_cast<bf16*>(dk);
   a.dv = static_cast<bf16*>(dv);
@@ -771,35 +782,35 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
   const int maxlen = g.cu ? g.max_doc_len : g.N;
   hipStream_t st = (hipStream_t)stream;
 
-  const int tpb = kDeltaPasses * kThreads / (g.d / 8);  // tokens per block
-  const dim3 dgrid((unsigned)((g.N + tpb - 1) / tpb), (unsigned)(a.units < 65535 ? a.units : 65535));
-
   BwdArgs aq = a;
   aq.nslots = (maxlen + kDqBQ - 1) / kDqBQ;
   const long long qblocks = (long long)aq.nslots * a.ndoc * a.units;
   BwdArgs akv = a;
   akv.nslots = (maxlen + kKvBK - 1) / kKvBK;
   const long long kvblocks = (long long)akv.nslots * a.ndoc * a.units;
-  // the tile decode also forms nslots * ndoc * kUnitGroup in int
-  const long long span_q = (long long)aq.nslots * a.ndoc * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
-  const long long span_kv = (long long)akv.nslots * a.ndoc * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
-  if (span_q > 0x7fffffffLL || span_kv > 0x7fffffffLL) return ULY_ESHAPE;
 
   if (g.d == 64) {
-    hipLaunchKernelGGL(delta_bf16_kernel<64>, dgrid, dim3(kThreads), 0, st, a.o, a.dout,
-                       lse, delta, a.lse2, g.N, g.Hl, (long long)a.units);
     hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL((attn_dq_bf16_kernel<64, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   } else {
-    hipLaunchKernelGGL(delta_bf16_kernel<128>, dgrid, dim3(kThreads), 0, st, a.o, a.dout,
-                       lse, delta, a.lse2, g.N, g.Hl, (long long)a.units);
     hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
     hipLaunchKernelGGL((attn_dq_bf16_kernel<128, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
   }
   return launch_status();
 }
 
-int launch_ring_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
+int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                         float* delta, const AttnGeom& g, void* stream) {
+  if (!bwd_tiles_fit(g)) return ULY_ESHAPE;  // before the pre-pass is enqueued
+  const int rc = launch_attn_bwd_prepare_bf16(o, dout, lse, delta, g, stream);
+  if (rc != ULY_OK) return rc;
+  return launch_attn_bwd_main_bf16(q, k, v, dout, lse, dq, dk, dv, delta, g, stream);
+}
+
+// The D pre-pass over G rows of N tokens and Hl heads: -D and lse * log2(e)
+// into the workspace (Ulysses shares and ring chunks alike).
+int launch_attn_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
                                  const AttnGeom& g, void* stream) {
   const long long rows = (long long)g.G * g.Hl * g.N;
   const long long units = (long long)g.G * g.Hl;
@@ -901,6 +912,59 @@ extern "C" int ulysses_attn_bwd(const void* q, const void* k, const void* v, con
         static_cast<const float*>(o), static_cast<const float*>(dout), lse, static_cast<float*>(dq),
         static_cast<float*>(dk), static_cast<float*>(dv), delta, g, stream);
   return uly_host::launch_attn_bwd_bf16(q, k, v, o, dout, lse, dq, dk, dv, delta, g, stream);
+}
+
+namespace {
+
+// Host checks of the split backward's calls; fills the geometry.
+int bwd_split_args(const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B, int N, int Hl, int d,
+                   int causal, int dtype, size_t workspace_bytes, const void* workspace, uly_host::AttnGeom& g) {
+  const int rc = uly_host::check_attn_args(ndoc, max_doc_len, cu_seqlens, sp, B, N, Hl, d, dtype);
+  if (rc != ULY_OK) return rc;
+  if (!workspace || workspace_bytes < ulysses_attn_bwd_workspace_bytes(sp, B, N, Hl, d, dtype)) return ULY_EWORKSPACE;
+  g.G = sp * B;
+  g.N = N;
+  g.Hl = Hl;
+  g.d = d;
+  g.cu = cu_seqlens;
+  g.ndoc = cu_seqlens ? ndoc : 1;
+  g.max_doc_len = cu_seqlens ? max_doc_len : N;
+  g.causal = causal ? 1 : 0;
+  return ULY_OK;
+}
+
+}  // namespace
+
+extern "C" int ulysses_attn_bwd_prepare(const void* o, const void* dout, const float* lse, void* workspace,
+                                        size_t workspace_bytes, int sp, int B, int N, int Hl, int d, int dtype,
+                                        void* stream) {
+  if (!o || !dout || !lse) return ULY_EINVAL;
+  uly_host::AttnGeom g;
+  const int rc = bwd_split_args(nullptr, 1, N, sp, B, N, Hl, d, 1, dtype, workspace_bytes, workspace, g);
+  if (rc != ULY_OK) return rc;
+  float* delta = static_cast<float*>(workspace);
+  if (dtype == ULY_F32)
+    return uly_host::launch_attn_bwd_prepare_f32(static_cast<const float*>(o), static_cast<const float*>(dout),
+                                                 delta, g, stream);
+  return uly_host::launch_attn_bwd_prepare_bf16(o, dout, lse, delta, g, stream);
+}
+
+extern "C" int ulysses_attn_bwd_prepared(const void* q, const void* k, const void* v, const void* dout,
+                                         const float* lse, void* dq, void* dk, void* dv, const void* workspace,
+                                         size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len,
+                                         int sp, int B, int N, int Hl, int d, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv) return ULY_EINVAL;
+  uly_host::AttnGeom g;
+  const int rc = bwd_split_args(cu_seqlens, ndoc, max_doc_len, sp, B, N, Hl, d, causal, dtype, workspace_bytes,
+                                workspace, g);
+  if (rc != ULY_OK) return rc;
+  const float* delta = static_cast<const float*>(workspace);
+  if (dtype == ULY_F32)
+    return uly_host::launch_attn_bwd_main_f32(
+        static_cast<const float*>(q), static_cast<const float*>(k), static_cast<const float*>(v),
+        static_cast<const float*>(dout), lse, static_cast<float*>(dq), static_cast<float*>(dk),
+        static_cast<float*>(dv), delta, g, stream);
+  return uly_host::launch_attn_bwd_main_bf16(q, k, v, dout, lse, dq, dk, dv, delta, g, stream);
 }
 
 // ----------------------------------------------------- no-allocation variant

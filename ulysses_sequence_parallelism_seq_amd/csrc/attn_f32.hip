@@ -252,27 +252,45 @@ int launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o
   return launch_status();
 }
 
-int launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
-                        const float* dout, const float* lse, float* dq, float* dk, float* dv,
-                        float* delta, const AttnGeom& a, void* stream) {
+int launch_attn_bwd_prepare_f32(const float* o, const float* dout, float* delta, const AttnGeom& a,
+                                void* stream) {
+  const int units = a.G * a.Hl;
+  hipStream_t st = (hipStream_t)stream;
+  const dim3 grid(row_blocks(a)), block(64 * kWaves);
+  if (a.d == 64)
+    hipLaunchKernelGGL(delta_f32<64>, grid, block, 0, st, o, dout, delta, a.N, a.Hl, units);
+  else
+    hipLaunchKernelGGL(delta_f32<128>, grid, block, 0, st, o, dout, delta, a.N, a.Hl, units);
+  return launch_status();
+}
+
+int launch_attn_bwd_main_f32(const float* q, const float* k, const float* v, const float* dout,
+                             const float* lse, float* dq, float* dk, float* dv, const float* delta,
+                             const AttnGeom& a, void* stream) {
   const float scale = 1.0f / sqrtf((float)a.d);
   const int units = a.G * a.Hl;
   hipStream_t st = (hipStream_t)stream;
   const dim3 grid(row_blocks(a)), block(64 * kWaves);
   if (a.d == 64) {
-    hipLaunchKernelGGL(delta_f32<64>, grid, block, 0, st, o, dout, delta, a.N, a.Hl, units);
     hipLaunchKernelGGL(dq_f32<64>, grid, block, 0, st, q, k, v, dout, lse, delta, dq, a.cu, a.ndoc, a.N,
                        a.Hl, units, a.causal, scale);
     hipLaunchKernelGGL(dkdv_f32<64>, grid, block, 0, st, q, k, v, dout, lse, delta, dk, dv, a.cu, a.ndoc,
                        a.N, a.Hl, units, a.causal, scale);
   } else {
-    hipLaunchKernelGGL(delta_f32<128>, grid, block, 0, st, o, dout, delta, a.N, a.Hl, units);
     hipLaunchKernelGGL(dq_f32<128>, grid, block, 0, st, q, k, v, dout, lse, delta, dq, a.cu, a.ndoc, a.N,
                        a.Hl, units, a.causal, scale);
     hipLaunchKernelGGL(dkdv_f32<128>, grid, block, 0, st, q, k, v, dout, lse, delta, dk, dv, a.cu,
                        a.ndoc, a.N, a.Hl, units, a.causal, scale);
   }
   return launch_status();
+}
+
+int launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
+                        const float* dout, const float* lse, float* dq, float* dk, float* dv,
+                        float* delta, const AttnGeom& a, void* stream) {
+  const int rc = launch_attn_bwd_prepare_f32(o, dout, delta, a, stream);
+  if (rc != ULY_OK) return rc;
+  return launch_attn_bwd_main_f32(q, k, v, dout, lse, dq, dk, dv, delta, a, stream);
 }
 
 }  // namespace uly_host

@@ -21,18 +21,28 @@ int launch_attn_fwd_f32(const float* q, const float* k, const float* v, float* o
 int launch_attn_bwd_f32(const float* q, const float* k, const float* v, const float* o,
                         const float* dout, const float* lse, float* dq, float* dk, float* dv,
                         float* delta, const AttnGeom& a, void* stream);
+// The backward's two steps: the D pre-pass into the workspace, then the
+// dQ and dK/dV kernels reading it.
+int launch_attn_bwd_prepare_f32(const float* o, const float* dout, float* delta, const AttnGeom& a,
+                                void* stream);
+int launch_attn_bwd_main_f32(const float* q, const float* k, const float* v, const float* dout,
+                             const float* lse, float* dq, float* dk, float* dv, const float* delta,
+                             const AttnGeom& a, void* stream);
 
 int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                          const AttnGeom& a, void* stream);
 int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* delta, const AttnGeom& a, void* stream);
+int launch_attn_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
+                                 const AttnGeom& a, void* stream);
+int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
+                              const float* lse, void* dq, void* dk, void* dv, const float* delta,
+                              const AttnGeom& a, void* stream);
 
 // Ring attention steps (bf16): rows g = chunk * B + b of Ns tokens, H heads.
 int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* o_acc, float* lse,
                          const AttnGeom& a, int sp, int B, int step, void* stream);
-int launch_ring_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
-                                 const AttnGeom& a, void* stream);
 int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
                          const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
                          void* dv, const AttnGeom& a, int sp, int B, int step, void* stream);

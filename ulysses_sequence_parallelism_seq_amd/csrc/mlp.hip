@@ -307,14 +307,20 @@ struct MlpGeom {
   int T, h, I, tile;
 };
 
-// Host-side checks shared by the entry points; the workspace holds three
+// Host-side checks shared by the entry points (all before any launch); the workspace holds three
 // [tile][I] bf16 arrays of one tile: A, then U * silu'(G) and silu(G) (the
 // backward's factors, overwritten by dG and dU).
 int check_mlp(int tokens, int hidden, int inter, int tile) {
   if (tokens <= 0 || hidden <= 0 || inter <= 0 || tile <= 0) return ULY_EINVAL;
   if (hidden % kBN || inter % kBN) return ULY_ESHAPE;
   // 32-bit buffer ranges and lane offsets: a staged tile spans < 2 GiB
-  if ((long long)kBM * 2 * (hidden > inter ? hidden : inter) >= (1LL << 31)) return ULY_ESHAPE;
+  const long long wide = hidden > inter ? hidden : inter;
+  if ((long long)kBM * 2 * wide >= (1LL << 31)) return ULY_ESHAPE;
+  // every launch's grid (row tiles x column tiles) fits, so no call stops
+  // with an error after some of its launches were enqueued
+  const long long rows = tile < tokens ? tile : tokens;
+  const long long tall = rows > wide ? rows : wide;
+  if ((tall + kBM - 1) / kBM * (wide / (kBN / 2)) > 0x7fffffffLL) return ULY_ESHAPE;
   return ULY_OK;
 }
 

@@ -171,7 +171,7 @@ extern "C" const char* ulysses_status_string(int status) {
   switch (status) {
     case ULY_OK: return "ok";
     case ULY_EINVAL: return "invalid argument (null pointer, size <= 0, overlapping or misaligned buffers, or step out of range)";
-    case ULY_ESHAPE: return "inconsistent shape (N % sp, H % sp, max_doc_len > N, or size limits)";
+    case ULY_ESHAPE: return "a size condition of the call fails (N % sp, H % sp, max_doc_len > N, or a size limit listed in ulysses.h)";
     case ULY_EUNSUPPORTED: return "unsupported dtype or head dimension (d must be 64 or 128)";
     case ULY_EWORKSPACE: return "workspace missing or too small";
     case ULY_EHIP: return "HIP runtime error while launching";

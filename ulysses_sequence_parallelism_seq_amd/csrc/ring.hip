@@ -69,7 +69,7 @@ extern "C" int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, co
   if (rc != ULY_OK) return rc;
   if (!workspace || workspace_bytes < ulysses_ring_attn_bwd_workspace_bytes(sp, B, Ns, H, d, dtype))
     return ULY_EWORKSPACE;
-  return uly_host::launch_ring_bwd_prepare_bf16(o, dout, lse, static_cast<float*>(workspace),
+  return uly_host::launch_attn_bwd_prepare_bf16(o, dout, lse, static_cast<float*>(workspace),
                                                 ring_geom(sp, B, Ns, H, d, 1), stream);
 }
 

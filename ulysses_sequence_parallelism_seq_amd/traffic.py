@@ -2,11 +2,15 @@
 
 Two counter runs of bench.py (one with FETCH_SIZE, one with WRITE_SIZE, in
 KiB per dispatch) give the bytes each kernel moved between L2 and memory. The
-counters are calibrated with the permute kernel of the same run, a plain copy
-whose bytes are known (it reads and writes every element once), and the
-figures are stored with a hash of the compiled library they were taken with,
-so that any change of its code invalidates them (and an edit that leaves the
-compiled code byte-identical, such as a comment, does not).
+counters are calibrated with a plain device-to-device copy of known size in
+the same run (bench.py copies one 1 GiB input tensor with torch's copy_, which
+runs the HIP runtime's own copy kernel: it reads and writes every byte once),
+independently of this library's kernels. The calibrated figures cover the
+backward's kernels (the roofline's "traffic") and the two permute kernels
+(their HBM bytes against the algorithmic read + write of every element). They
+are stored with a hash of the compiled library they were taken with, so that
+any change of its code invalidates them (and an edit that leaves the compiled
+code byte-identical, such as a comment, does not).
 
   python -m ulysses_sequence_parallelism_seq_amd.traffic FETCH_DIR WRITE_DIR OUT.txt "COMMANDS"
 
@@ -25,7 +29,8 @@ import sys
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(_HERE, "libulysses.so")
 BWD_KERNELS = ("attn_dkdv_bf16_kernel<128,false>", "attn_dq_bf16_kernel<128,false>", "delta_bf16_kernel<128>")
-COPY_KERNEL = "permute_seq_to_head"
+PERMUTE_KERNELS = ("permute_seq_to_head", "permute_head_to_seq")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
 
 
 def library_sha256() -> str | None:
@@ -48,16 +53,24 @@ def _short(name: str) -> str:
 
 
 def _per_dispatch(csv_dir: str, counter: str) -> dict:
-    sums, counts = {}, {}
+    """Average counter value per dispatch of each kernel. For the runtime's copy
+    kernel only the dispatches of the largest grid (the calibration copies of
+    one whole tensor) count."""
+    values = {}
     for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
             for row in csv.DictReader(f):
                 if row["Counter_Name"] != counter:
                     continue
                 k = _short(row["Kernel_Name"])
-                sums[k] = sums.get(k, 0.0) + float(row["Counter_Value"])
-                counts[k] = counts.get(k, 0) + 1
-    return {k: sums[k] / counts[k] for k in sums}
+                values.setdefault(k, []).append((int(row.get("Grid_Size") or 0), float(row["Counter_Value"])))
+    out = {}
+    for k, vs in values.items():
+        if k == COPY_KERNEL:
+            g = max(gs for gs, _ in vs)
+            vs = [x for x in vs if x[0] == g]
+        out[k] = sum(v for _, v in vs) / len(vs)
+    return out
 
 
 def write_traffic(fetch_dir: str, write_dir: str, out: str, commands: str, copy_bytes: int) -> None:
@@ -71,12 +84,16 @@ def write_traffic(fetch_dir: str, write_dir: str, out: str, commands: str, copy_
     ]
     for k in BWD_KERNELS:
         lines.append(f"kernel {k} fetch_kib={fetch[k]:.1f} write_kib={write[k]:.1f}")
+    for k in PERMUTE_KERNELS:
+        lines.append(f"permute {k} fetch_kib={fetch[k]:.1f} write_kib={write[k]:.1f}")
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
 def read_traffic(path: str):
-    """Calibrated bytes of one attention-backward call, or None if stale or missing."""
+    """Calibrated HBM bytes of one attention-backward call ("bytes") and of one
+    call of each permute kernel ("permute": name -> bytes), or None if the
+    figures are stale or missing."""
     if not os.path.exists(path):
         return None
     rec = {}
@@ -87,7 +104,7 @@ def read_traffic(path: str):
                 continue
             if parts[0] == "library_sha256":
                 rec["sha"] = parts[1]
-            elif parts[0] in ("copy", "kernel"):
+            elif parts[0] in ("copy", "kernel", "permute"):
                 rec[(parts[0], parts[1])] = dict(p.split("=") for p in parts[2:])
     if rec.get("sha") is None or rec.get("sha") != library_sha256():
         return None
@@ -97,10 +114,14 @@ def read_traffic(path: str):
     f_scale = copy_kib / float(copy["fetch_kib"])
     w_scale = copy_kib / float(copy["write_kib"])
     total = 0.0
-    for (kind, _), v in entries:
+    permute = {}
+    for (kind, name), v in entries:
+        kib = float(v["fetch_kib"]) * f_scale + float(v["write_kib"]) * w_scale
         if kind == "kernel":
-            total += float(v["fetch_kib"]) * f_scale + float(v["write_kib"]) * w_scale
-    return {"bytes": total * 1024.0, "fetch_scale": f_scale, "write_scale": w_scale}
+            total += kib
+        elif kind == "permute":
+            permute[name] = kib * 1024.0
+    return {"bytes": total * 1024.0, "fetch_scale": f_scale, "write_scale": w_scale, "permute": permute}
 
 
 if __name__ == "__main__":
