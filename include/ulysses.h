@@ -121,7 +121,11 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float
 /*
  * Bytes of device workspace ulysses_attn_bwd needs: two floats per (rank,
  * batch row, head, token) (the row sums D = rowsum(dO * O), stored negated,
- * and lse in log2 units), i.e. O(N), never O(N^2). Returns 0 for invalid arguments.
+ * and lse in log2 units), i.e. O(N), never O(N^2), rounded up to 256 bytes,
+ * plus 256 bytes of tile-queue counters for the bf16 kernels (they run one
+ * workgroup per compute unit, each taking tiles until none is left; the
+ * pre-pass clears the counters and every kernel leaves them cleared).
+ * Returns 0 for invalid arguments.
  */
 size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype);
 
@@ -157,14 +161,16 @@ int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
  *     only; the values do not depend on the packing.
  *   ulysses_attn_bwd_prepared: the dK/dV and dQ kernels, reading the
  *     workspace a prepare call of the same sizes and dtype filled (its
- *     contents are not checked); q, k, v, dout, lse, dq, dk, dv, cu_seqlens,
- *     ndoc, max_doc_len, causal as in ulysses_attn_bwd.
+ *     contents are not checked; the kernels claim their tiles through the
+ *     counters at its end and leave them cleared, so one prepare may serve
+ *     several prepared calls in turn); q, k, v, dout, lse, dq, dk, dv,
+ *     cu_seqlens, ndoc, max_doc_len, causal as in ulysses_attn_bwd.
  * Errors: as ulysses_attn_bwd.
  */
 int ulysses_attn_bwd_prepare(const void* o, const void* dout, const float* lse, void* workspace,
                              size_t workspace_bytes, int sp, int B, int N, int Hl, int d, int dtype, void* stream);
 int ulysses_attn_bwd_prepared(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                              void* dq, void* dk, void* dv, const void* workspace, size_t workspace_bytes,
+                              void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                               const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B, int N, int Hl,
                               int d, int causal, int dtype, void* stream);
 
@@ -189,7 +195,7 @@ int ulysses_attn_bwd_prepared(const void* q, const void* k, const void* v, const
  * scratch than the limit; ULY_EHIP when the scratch's device address cannot
  * be looked up.
  */
-#define ULY_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define ULY_NOALLOC_SCRATCH_BYTES (((size_t)64 << 20) + 256)
 int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
                              const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int ndoc,
                              int max_doc_len, int sp, int B, int N, int Hl, int d, int causal, int dtype,

@@ -82,7 +82,9 @@ def test_attention_argument_errors():
 
     bwd = lib.ulysses_attn_bwd
     need = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 64, 1)
-    assert need == 2 * 1 * 1 * 2 * 8 * 4  # D and lse in log2 units, one float each per (unit, token)
+    # D and lse in log2 units, one float each per (unit, token), rounded up to 256 bytes,
+    # then 256 bytes of tile-queue counters
+    assert need == (2 * 1 * 1 * 2 * 8 * 4 + 255) // 256 * 256 + 256
     assert lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 48, 1) == 0
     ptrs = [FAKE] * 9
     assert bwd(*ptrs, FAKE, need - 1, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
@@ -106,17 +108,21 @@ def test_noalloc_argument_errors():
 
 def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
-    m = re.search(r"#define ULY_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    m = re.search(r"#define ULY_NOALLOC_SCRATCH_BYTES \(\(\(size_t\)(\d+) << (\d+)\) \+ (\d+)\)", text)
     assert m, "ULY_NOALLOC_SCRATCH_BYTES not found in the header"
-    assert int(m.group(1)) << int(m.group(2)) == uly.ULY_NOALLOC_SCRATCH_BYTES
-    # the limit in rows stated in the header: two floats per (token, head) row
-    assert uly.ULY_NOALLOC_SCRATCH_BYTES // 8 == 8388608
+    assert (int(m.group(1)) << int(m.group(2))) + int(m.group(3)) == uly.ULY_NOALLOC_SCRATCH_BYTES
+    # the limit in rows stated in the header: two floats per (token, head) row, plus the
+    # 256 bytes of tile-queue counters
+    assert (uly.ULY_NOALLOC_SCRATCH_BYTES - 256) // 8 == 8388608
+    lib = uly.library()
+    assert lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8388608, 1, 64, 1) == uly.ULY_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_is_linear_in_n():
+    """O(N) workspace: two floats per (unit, token) plus a fixed 256 bytes of queue counters."""
     lib = uly.library()
-    w1 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 131072, 4, 128, 1)
-    w2 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 262144, 4, 128, 1)
+    w1 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 131072, 4, 128, 1) - 256
+    w2 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 262144, 4, 128, 1) - 256
     assert w2 == 2 * w1 == 2 * 2 * 131072 * 4 * 4
 
 

@@ -71,6 +71,14 @@ struct BwdArgs {
   float* dk_acc;
   float* dv_acc;
   int step, sp, B;
+  // persistent launch: the kernel's tile-queue counters (TileQueue), in the
+  // workspace; nullptr: one tile per workgroup
+  int* sched;
+};
+
+template <bool B>
+struct RoleTag {
+  static constexpr bool value = B;
 };
 
 // Ring step geometry of a row g = c * B + b whose chunk c is held by the
@@ -114,6 +122,10 @@ __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int
 // tokens; each group of D/8 lanes takes kDeltaPasses rows, all loads (non-temporal:
 // O and dO stream through once) issued before the first product.
 constexpr int kDeltaPasses = 4;
+// Tile-queue counters of a persistent backward, at the end of the workspace:
+// the dK/dV kernel's at [0, kQueueInts), the dQ kernel's at [16, 16 + kQueueInts).
+constexpr int kSchedInts = 32;
+constexpr int kSchedDq = 16;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt16(const bf16* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
@@ -125,7 +137,9 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
                                                               const float* __restrict__ lse,
                                                               float* __restrict__ delta,
                                                               float* __restrict__ lse2, int N, int Hl,
-                                                              long long units) {
+                                                              long long units, int* __restrict__ sched) {
+  // the tile-queue counters of the dK/dV and dQ kernels start at zero
+  if (sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kSchedInts) sched[threadIdx.x] = 0;
   constexpr int LPR = D / 8;              // lanes per row
   constexpr int RPP = kThreads / LPR;     // rows per pass
   const int sub = threadIdx.x % LPR;
@@ -203,162 +217,172 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
   __shared__ __attribute__((aligned(16))) bf16 k1s[TILE];
   __shared__ __attribute__((aligned(16))) bf16 v1s[TILE];
 
-  const TileId tid_ = decode_tile(blockIdx.x, a.nslots, a.ndoc, a.units);
-  const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
-  int s, e;
-  doc_range(a, doc, s, e);
-  const int q0 = s + (a.nslots - 1 - lvl) * kDqBQ;
-  if (q0 >= e) return;  // the whole workgroup leaves before any barrier
+  __shared__ int s_claim[2];
+  TileQueue tq;
+  tq.init(a.sched, a.nslots, a.ndoc, a.units);
+  TileId tid_;
+  while (tq.next(tid_, s_claim)) {
+    const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
+    int s, e;
+    doc_range(a, doc, s, e);
+    const int q0 = s + (a.nslots - 1 - lvl) * kDqBQ;
+    if (q0 >= e) continue;  // the whole workgroup skips the tile
 
-  const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
-  const size_t rs = (size_t)a.Hl * D;
-  const uint32_t row_bytes = (uint32_t)rs * 2u;
-  const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
-  size_t kvbase = base;
-  int causal = a.causal;
-  RingBlock rb{g, a.causal, true, true};
-  if constexpr (kRing) {
-    if (!ring_block(a, g, true, rb)) return;  // before any barrier
-    causal = rb.causal;
-    kvbase = ((size_t)rb.other * a.N * a.Hl + hd) * D;
-  }
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const int qi = q0 + 32 * w + l32;
-  const bool qvalid = qi < e;
-  FragOffsets<D> fo;
-  fo.init(lane);
-
-  // Q^T and dO^T as resident B operands (rows past the document end read as zero)
-  uint4 qreg[KK], doreg[KK];
-  {
-    const long long span = (long long)(e - q0) * row_bytes;
-    const rsrc_t qr = make_rsrc(a.q + base + (size_t)q0 * rs, span);
-    const rsrc_t dr = make_rsrc(a.dout + base + (size_t)q0 * rs, span);
-    const uint32_t off = (uint32_t)(32 * w + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      qreg[kk] = buf_load16(qr, off + 32u * kk);
-      doreg[kk] = buf_load16(dr, off + 32u * kk);
+    const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
+    const size_t rs = (size_t)a.Hl * D;
+    const uint32_t row_bytes = (uint32_t)rs * 2u;
+    const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
+    size_t kvbase = base;
+    int causal = a.causal;
+    RingBlock rb{g, a.causal, true, true};
+    if constexpr (kRing) {
+      if (!ring_block(a, g, true, rb)) continue;  // the whole workgroup skips the tile
+      causal = rb.causal;
+      kvbase = ((size_t)rb.other * a.N * a.Hl + hd) * D;
     }
-  }
-  const float lse2 = qvalid ? a.lse[(size_t)unit * a.N + qi] * kLog2e : 0.f;
-  const float ndlt = qvalid ? a.delta[(size_t)unit * a.N + qi] : 0.f;  // -D
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int qi = q0 + 32 * w + l32;
+    const bool qvalid = qi < e;
+    FragOffsets<D> fo;
+    fo.init(lane);
 
-  const int kend = causal ? min(e, q0 + kDqBQ) : e;
-  const int ntiles = (kend - s + kDqBK - 1) / kDqBK;
-
-  f32x16 dqacc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) dqacc[cb][i] = 0.f;
-
-  auto rsrc_at = [&](const bf16* p, int kt0) {
-    return make_rsrc(p + kvbase + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
-  };
-  // K/V tiles by direct-to-LDS loads: tile t+1 goes out before the math of
-  // tile t and is waited for before its barrier
-  TileDma<D, kDqBK, kDqThreads / 64> dma;
-  dma.init(w, lane, row_bytes);
-  dma.issue(rsrc_at(a.k, s), k0s);
-  dma.issue(rsrc_at(a.v, s), v0s);
-  wait_vmem();
-  __syncthreads();
-
-  auto step = [&](int t, const bf16* ks, const bf16* vs, const bf16* kn, const bf16* vn) {
-    const int kt0 = s + t * kDqBK;
-    if (t + 1 < ntiles) {
-      dma.issue(rsrc_at(a.k, kt0 + kDqBK), kn);
-      dma.issue(rsrc_at(a.v, kt0 + kDqBK), vn);
-    }
-
-    if (!causal || kt0 <= q0 + 32 * w + 31) {
-      const bool need_mask = (causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
-      // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (lane = query,
-      // element i is key kt0 + blk*32 + 8*(i/4) + 4*half + (i%4)), dS^T, then
-      // dQ^T += K^T dS^T with K^T read from the K tile by transposing reads
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        f32x16 sacc, pacc;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
-        // K and V fragments read two k-steps ahead of their MFMAs
-        auto rd = [&](int kk, uint4* f) {
-          const uint32_t off = fo.row_frag(blk, kk);
-          f[0] = lds_ld16(ks, off);
-          f[1] = lds_ld16(vs, off);
-        };
-        uint4 fr[3][2];
-        rd(0, fr[0]);
-        rd(1, fr[1]);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 2 < KK) rd(kk + 2, fr[(kk + 2) % 3]);
-          sacc = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(qreg[kk]), sacc);
-          pacc = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(doreg[kk]), pacc);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // K^T operands of the dQ MFMAs go out now and land during the exponentials
-        bf16x8 kt[CB][2];
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm) kt[cb][mm] = a_from_rows_at<D>(ks, fo, 2 * blk + mm, cb);
-        if (need_mask) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= e || (causal && key > qi)) sacc[i] = -INFINITY;
-          }
-        }
-        uint4 dsb[2];
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          float ds[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int i = 8 * mm + j;
-            ds[j] = fast_exp2(fmaf(sacc[i], a.sl2, -lse2)) * (pacc[i] + ndlt);
-          }
-          dsb[mm] = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
-                               pack_bf16x2(ds[6], ds[7]));
-        }
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-            dqacc[cb] = mfma32(kt[cb][mm], as_bf16x8(dsb[mm]), dqacc[cb]);
+    // Q^T and dO^T as resident B operands (rows past the document end read as zero)
+    uint4 qreg[KK], doreg[KK];
+    {
+      const long long span = (long long)(e - q0) * row_bytes;
+      const rsrc_t qr = make_rsrc(a.q + base + (size_t)q0 * rs, span);
+      const rsrc_t dr = make_rsrc(a.dout + base + (size_t)q0 * rs, span);
+      const uint32_t off = (uint32_t)(32 * w + l32) * row_bytes + (uint32_t)(8 * half) * 2u;
+  #pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        qreg[kk] = buf_load16(qr, off + 32u * kk);
+        doreg[kk] = buf_load16(dr, off + 32u * kk);
       }
     }
+    const float lse2 = qvalid ? a.lse[(size_t)unit * a.N + qi] * kLog2e : 0.f;
+    const float ndlt = qvalid ? a.delta[(size_t)unit * a.N + qi] : 0.f;  // -D
 
+    const int kend = causal ? min(e, q0 + kDqBQ) : e;
+    const int ntiles = (kend - s + kDqBK - 1) / kDqBK;
+
+    f32x16 dqacc[CB];
+  #pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+      for (int i = 0; i < 16; ++i) dqacc[cb][i] = 0.f;
+
+    auto rsrc_at = [&](const bf16* p, int kt0) {
+      return make_rsrc(p + kvbase + (size_t)kt0 * rs, (long long)(e - kt0) * row_bytes);
+    };
+    // K/V tiles by direct-to-LDS loads: tile t+1 goes out before the math of
+    // tile t and is waited for before its barrier
+    TileDma<D, kDqBK, kDqThreads / 64> dma;
+    dma.init(w, lane, row_bytes);
+    dma.issue(rsrc_at(a.k, s), k0s);
+    dma.issue(rsrc_at(a.v, s), v0s);
     wait_vmem();
     __syncthreads();
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, k0s, v0s, k1s, v1s);
-    if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
-  }
 
-  if (qvalid) {
-    bf16* out = a.dq + base + (size_t)qi * rs;
-    if constexpr (kRing) {
-      float* acc = a.dq_acc + base + (size_t)qi * rs;
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int c = cb * 32 + 8 * gq + 4 * half;
-          add_store4(acc + c, dqacc[cb], 4 * gq, a.scale, rb.first, rb.last ? out + c : nullptr);
+    auto step = [&](int t, const bf16* ks, const bf16* vs, const bf16* kn, const bf16* vn) {
+      const int kt0 = s + t * kDqBK;
+      if (t + 1 < ntiles) {
+        dma.issue(rsrc_at(a.k, kt0 + kDqBK), kn);
+        dma.issue(rsrc_at(a.v, kt0 + kDqBK), vn);
+      }
+
+      if (!causal || kt0 <= q0 + 32 * w + 31) {
+        const bool need_mask = (causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
+        // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (lane = query,
+        // element i is key kt0 + blk*32 + 8*(i/4) + 4*half + (i%4)), dS^T, then
+        // dQ^T += K^T dS^T with K^T read from the K tile by transposing reads
+  #pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+          f32x16 sacc, pacc;
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) sacc[i] = pacc[i] = 0.f;
+          // K and V fragments read two k-steps ahead of their MFMAs
+          auto rd = [&](int kk, uint4* f) {
+            const uint32_t off = fo.row_frag(blk, kk);
+            f[0] = lds_ld16(ks, off);
+            f[1] = lds_ld16(vs, off);
+          };
+          uint4 fr[3][2];
+          rd(0, fr[0]);
+          rd(1, fr[1]);
+  #pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) rd(kk + 2, fr[(kk + 2) % 3]);
+            // the reads go out before this step's MFMAs (the scheduler would
+            // otherwise start the block's first MFMA after one read only)
+            __builtin_amdgcn_sched_barrier(0);
+            sacc = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(qreg[kk]), sacc);
+            pacc = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(doreg[kk]), pacc);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // K^T operands of the dQ MFMAs go out now and land during the exponentials
+          bf16x8 kt[CB][2];
+  #pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+            for (int mm = 0; mm < 2; ++mm) kt[cb][mm] = a_from_rows_at<D>(ks, fo, 2 * blk + mm, cb);
+          if (need_mask) {
+  #pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int key = kt0 + blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+              if (key >= e || (causal && key > qi)) sacc[i] = -INFINITY;
+            }
+          }
+          uint4 dsb[2];
+  #pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            float ds[8];
+  #pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const int i = 8 * mm + j;
+              ds[j] = fast_exp2(fmaf(sacc[i], a.sl2, -lse2)) * (pacc[i] + ndlt);
+            }
+            dsb[mm] = make_uint4(pack_bf16x2(ds[0], ds[1]), pack_bf16x2(ds[2], ds[3]), pack_bf16x2(ds[4], ds[5]),
+                                 pack_bf16x2(ds[6], ds[7]));
+          }
+  #pragma unroll
+          for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+              dqacc[cb] = mfma32(kt[cb][mm], as_bf16x8(dsb[mm]), dqacc[cb]);
         }
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          *reinterpret_cast<uint2*>(out + cb * 32 + 8 * gq + 4 * half) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
+      }
+
+      wait_vmem();
+      __syncthreads();
+    };
+    for (int t = 0; t < ntiles; t += 2) {
+      step(t, k0s, v0s, k1s, v1s);
+      if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
+    }
+
+    if (qvalid) {
+      bf16* out = a.dq + base + (size_t)qi * rs;
+      if constexpr (kRing) {
+        float* acc = a.dq_acc + base + (size_t)qi * rs;
+  #pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int c = cb * 32 + 8 * gq + 4 * half;
+            add_store4(acc + c, dqacc[cb], 4 * gq, a.scale, rb.first, rb.last ? out + c : nullptr);
+          }
+      } else {
+  #pragma unroll
+        for (int cb = 0; cb < CB; ++cb)
+  #pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<uint2*>(out + cb * 32 + 8 * gq + 4 * half) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
+      }
     }
   }
+  tq.finish();
 }
 
 // ------------------------------------------------------------------- dkdv kernel
@@ -448,302 +472,338 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   // P and dS of the last tile: per producer, per query block, 4 MFMA operands of 64 lanes
   __shared__ __attribute__((aligned(16))) uint4 xbuf[4 * 2 * 4 * 64];
 
-  const TileId tid_ = decode_tile(blockIdx.x, a.nslots, a.ndoc, a.units);
-  const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
-  int s, e;
-  doc_range(a, doc, s, e);
-  const int kb0 = s + lvl * kKvBK;  // causal: low key blocks have the most queries, so they go first
-  if (kb0 >= e) return;             // the whole workgroup leaves before any barrier
-
-  const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
-  const size_t rs = (size_t)a.Hl * D;
-  const uint32_t row_bytes = (uint32_t)rs * 2u;
-  const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
-  size_t qbase = base;
-  int qunit = unit;
-  int causal = a.causal;
-  RingBlock rb{g, a.causal, true, true};
-  if constexpr (kRing) {
-    if (!ring_block(a, g, false, rb)) return;  // before any barrier
-    causal = rb.causal;
-    qbase = ((size_t)rb.other * a.N * a.Hl + hd) * D;
-    qunit = rb.other * a.Hl + hd;
-  }
-  const int tid = threadIdx.x;
+  __shared__ int s_claim[2];
+  TileQueue tq;
+  tq.init(a.sched, a.nslots, a.ndoc, a.units);
   // The wave index is the same in every lane; saying so keeps the role
   // branches and the direct-to-LDS loads' LDS window (M0) scalar, where the
   // compiler would otherwise wrap each such load in a loop over the lanes'
   // distinct values (about 3% of this kernel's time).
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, half = lane >> 5, l32 = lane & 31;
-  const bool producer = w < 4;
-  const int pair = w & 3;
-  const int kp0 = kb0 + 32 * pair;  // the pair's first key
-  const int kj = kp0 + l32;         // this lane's key (producer waves)
-  FragOffsets<D> fo;
-  fo.init(lane);
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // One tile, for one role: producers and consumers run their own tile
+  // loops (their registers stay apart) through the same sequence of barriers.
+  auto tile = [&](const TileId& tid_, auto role) __attribute__((always_inline)) {
+    constexpr bool producer = decltype(role)::value;
+    const int lvl = tid_.lvl, doc = tid_.doc, unit = tid_.unit;
+    int s, e;
+    doc_range(a, doc, s, e);
+    const int kb0 = s + lvl * kKvBK;  // causal: low key blocks have the most queries, so they go first
+    if (kb0 >= e) return;             // the whole workgroup skips the tile
 
-  const int qstart = causal ? kb0 : s;
-  const int ntiles = (e - qstart + kKvBQ - 1) / kKvBQ;
-  // Query tiles are walked from the document end down: every workgroup of a
-  // head then reads the same tile at about the same time, from the XCD's L2.
-  const int qlast = qstart + (ntiles - 1) * kKvBQ;
-
-  KvDma<D> dma;
-  dma.init(w, lane, row_bytes);
-  const float* lse2_u = a.lse2 + (size_t)qunit * a.N;
-  const float* dl_u = a.delta + (size_t)qunit * a.N;
-  auto load_tile = [&](int i, KvStage<D>& st) {
-    const int qt0 = qlast - i * kKvBQ;
-    const long long span = (long long)(e - qt0) * row_bytes;
-    dma.issue(make_rsrc(a.q + qbase + (size_t)qt0 * rs, span), make_rsrc(a.dout + qbase + (size_t)qt0 * rs, span),
-              make_rsrc(lse2_u + qt0, (long long)(e - qt0) * 4), make_rsrc(dl_u + qt0, (long long)(e - qt0) * 4),
-              st, w, lane);
-  };
-
-  // The tile loop, with the three stages named per iteration (i mod 3):
-  // work(i, cur, prev) runs between the loads of tile i + 1 going out and the
-  // first barrier, publish(i) between the two barriers. Producers and
-  // consumers run it with their own bodies, so that each role's registers are
-  // its own; both pass the same barriers.
-  auto tile_loop = [&](auto work, auto publish) {
-    auto iteration = [&](int i, const KvStage<D>& cur, const KvStage<D>& prev, KvStage<D>& next) {
-      if (i + 1 < ntiles) load_tile(i + 1, next);
-      work(i, cur, prev);
-      barrier_lds_only();  // the consumer has read the P/dS buffer
-      publish(i);
-      wait_vmem();
-      __syncthreads();  // new P/dS and tile i + 1 visible
-    };
-    load_tile(0, st0);
-    wait_vmem();
-    __syncthreads();
-    for (int i = 0; i <= ntiles; i += 3) {
-      iteration(i, st0, st2, st1);
-      if (i + 1 <= ntiles) iteration(i + 1, st1, st0, st2);
-      if (i + 2 <= ntiles) iteration(i + 2, st2, st1, st0);
+    const int g = unit / a.Hl, hd = unit - (unit / a.Hl) * a.Hl;
+    const size_t rs = (size_t)a.Hl * D;
+    const uint32_t row_bytes = (uint32_t)rs * 2u;
+    const size_t base = ((size_t)g * a.N * a.Hl + hd) * D;
+    size_t qbase = base;
+    int qunit = unit;
+    int causal = a.causal;
+    RingBlock rb{g, a.causal, true, true};
+    if constexpr (kRing) {
+      if (!ring_block(a, g, false, rb)) return;  // the whole workgroup skips the tile
+      causal = rb.causal;
+      qbase = ((size_t)rb.other * a.N * a.Hl + hd) * D;
+      qunit = rb.other * a.Hl + hd;
     }
-  };
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+    const int pair = w & 3;
+    const int kp0 = kb0 + 32 * pair;  // the pair's first key
+    const int kj = kp0 + l32;         // this lane's key (producer waves)
+    FragOffsets<D> fo;
+    fo.init(lane);
 
-  if (producer) {
-    // K^T and V^T of the pair's 32 keys (zero past the document end)
-    uint4 kreg[KK], vreg[KK];
-    {
-      const long long span = (long long)(e - kp0) * row_bytes;
-      const rsrc_t kr = make_rsrc(a.k + base + (size_t)kp0 * rs, span);
-      const rsrc_t vr = make_rsrc(a.v + base + (size_t)kp0 * rs, span);
-      const uint32_t off = (uint32_t)l32 * row_bytes + (uint32_t)(8 * half) * 2u;
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        kreg[kk] = buf_load16(kr, off + 32u * kk);
-        vreg[kk] = buf_load16(vr, off + 32u * kk);
-      }
-    }
-    // P and dS of both query blocks as MFMA B operands: pk[4 qb + mm] = P,
-    // pk[4 qb + 2 + mm] = dS, accumulator elements 8 mm .. 8 mm + 7
-    uint4 pk[8];
-    auto produce = [&](int i, const KvStage<D>& st, const KvStage<D>&) {
-      if (i >= ntiles) return;
+    const int qstart = causal ? kb0 : s;
+    const int ntiles = (e - qstart + kKvBQ - 1) / kKvBQ;
+    // Query tiles are walked from the document end down: every workgroup of a
+    // head then reads the same tile at about the same time, from the XCD's L2.
+    const int qlast = qstart + (ntiles - 1) * kKvBQ;
+
+    KvDma<D> dma;
+    dma.init(w, lane, row_bytes);
+    const float* lse2_u = a.lse2 + (size_t)qunit * a.N;
+    const float* dl_u = a.delta + (size_t)qunit * a.N;
+    auto load_tile = [&](int i, KvStage<D>& st) {
       const int qt0 = qlast - i * kKvBQ;
-      // tiles that cross the diagonal or a document end are masked element by element
-      const bool need_mask = (causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
-      // S = Q K^T and dP = dO V^T of both 32-query blocks. The exponentials of
-      // block 0 run between the MFMAs of block 1, four elements every other
-      // k-step (their lse2 and D read one step before), so the wave's own
-      // matrix work covers half of its softmax.
-      // dP starts from -D of its queries (the pre-pass stores D negated), so
-      // the MFMAs leave dP - D and the softmax has no subtraction to do
-      f32x16 sacc[2], pacc[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const float4 d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
-          sacc[qb][4 * gq] = sacc[qb][4 * gq + 1] = sacc[qb][4 * gq + 2] = sacc[qb][4 * gq + 3] = 0.f;
-          pacc[qb][4 * gq] = d4.x;
-          pacc[qb][4 * gq + 1] = d4.y;
-          pacc[qb][4 * gq + 2] = d4.z;
-          pacc[qb][4 * gq + 3] = d4.w;
-        }
-      }
-      // Q and dO fragments read two k-steps ahead of their MFMAs
-      auto rd = [&](int qb, int kk, uint4* f) {
-        const uint32_t off = fo.row_frag(qb, kk);
-        f[0] = lds_ld16(st.q, off);
-        f[1] = lds_ld16(st.dout, off);
-      };
-      // lse2 of the four queries of accumulator elements 4 gq .. 4 gq + 3
-      auto rd_ld = [&](int qb, int gq, float4& l4) {
-        l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
-      };
-      // in place: sacc becomes P
-      auto soft4 = [&](int qb, int gq, const float4& l4) {
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-#pragma unroll
-        for (int x = 0; x < 4; ++x) {
-          const int i2 = 4 * gq + x;
-          sacc[qb][i2] = fast_exp2(fmaf(sacc[qb][i2], a.sl2, -lv[x]));
-        }
-      };
-      // masked P (zero where the key is not visible to the query) and P (dP - D)
-      // of accumulator elements 8 mm .. 8 mm + 7 of block qb, packed to bf16
-      auto pack8 = [&](int qb, int mm) {
-        const int b = 8 * mm;
-        if (need_mask) {
-#pragma unroll
-          for (int x = b; x < b + 8; ++x) {
-            const int qq = qt0 + 32 * qb + 8 * (x >> 2) + 4 * half + (x & 3);
-            if (qq >= e || kj >= e || (causal && kj > qq)) sacc[qb][x] = 0.f;
-          }
-        }
-        const f32x16& p = sacc[qb];
-        const f32x16& ds = pacc[qb];
-        pk[4 * qb + mm] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
-                                     pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
-        pk[4 * qb + 2 + mm] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
-                                         pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
-                                         pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
-                                         pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
-      };
-      {
-        uint4 fr[3][2];
-        rd(0, 0, fr[0]);
-        rd(0, 1, fr[1]);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 2 < KK) rd(0, kk + 2, fr[(kk + 2) % 3]);
-          sacc[0] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[0]);
-          pacc[0] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[0]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
-      {
-        uint4 fr[3][2];
-        float4 l4;
-        rd(1, 0, fr[0]);
-        rd(1, 1, fr[1]);
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if (kk + 2 < KK) rd(1, kk + 2, fr[(kk + 2) % 3]);
-          if ((kk & 1) == 0 && kk / 2 < 4) rd_ld(0, kk / 2, l4);
-          sacc[1] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[1]);
-          pacc[1] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[1]);
-          if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2, l4);
-          if (kk == 3 || kk == 7) pack8(0, kk / 4);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // with D = 64 there are only four k-steps: the rest of block 0 here
-#pragma unroll
-        for (int gq = KK / 2; gq < 4; ++gq) {
-          rd_ld(0, gq, l4);
-          soft4(0, gq, l4);
-        }
-        if (KK < 8) pack8(0, 1);
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          rd_ld(1, gq, l4);
-          soft4(1, gq, l4);
-        }
-      }
-#pragma unroll
-      for (int mm = 0; mm < 2; ++mm) pack8(1, mm);
+      const long long span = (long long)(e - qt0) * row_bytes;
+      dma.issue(make_rsrc(a.q + qbase + (size_t)qt0 * rs, span), make_rsrc(a.dout + qbase + (size_t)qt0 * rs, span),
+                make_rsrc(lse2_u + qt0, (long long)(e - qt0) * 4), make_rsrc(dl_u + qt0, (long long)(e - qt0) * 4),
+                st, w, lane);
     };
-    auto publish = [&](int i) {
-      if (i >= ntiles) return;
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xbuf[((pair * 2 + qb) * 4 + j) * 64 + lane] = pk[4 * qb + j];
-    };
-    tile_loop(produce, publish);
-  } else {
-    // Consumer c takes the P/dS of producer pairs 2 (c/2) and 2 (c/2) + 1 (64
-    // keys) and accumulates dK^T, dV^T for half of the D columns, those of
-    // column blocks CH (c % 2) .. CH (c % 2) + CH - 1: every A fragment (dO^T,
-    // Q^T) it reads serves both key blocks and every P/dS operand both column
-    // blocks.
-    constexpr int CH = CB / 2;
-    const int kp_first = 2 * (pair >> 1);  // first producer pair of this consumer
-    const int cb0 = CH * (pair & 1);
-    f32x16 dkacc[2][CH], dvacc[2][CH];  // [key block][column block]
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) dkacc[kb][c][i] = dvacc[kb][c][i] = 0.f;
-    // the previous tile, in four steps (query block qb, 16-query half hf):
-    // A = dO^T, Q^T of those 16 queries for the CH column blocks, B = P, dS
-    // of the two key blocks; the next step's operands are read while this
-    // step's MFMAs run
-    auto consume = [&](int i, const KvStage<D>&, const KvStage<D>& st) {
-      if (i < 1) return;
-      auto rd = [&](int step, bf16x8 (*fa)[2], uint4 (*fb)[2]) {
-        const int qb = step >> 1, hf = step & 1;
-#pragma unroll
-        for (int c = 0; c < CH; ++c) {
-          fa[c][0] = a_from_rows_at<D>(st.dout, fo, 2 * qb + hf, cb0 + c);
-          fa[c][1] = a_from_rows_at<D>(st.q, fo, 2 * qb + hf, cb0 + c);
-        }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          fb[kb][0] = xbuf[(((kp_first + kb) * 2 + qb) * 4 + hf) * 64 + lane];
-          fb[kb][1] = xbuf[(((kp_first + kb) * 2 + qb) * 4 + 2 + hf) * 64 + lane];
-        }
-      };
-      bf16x8 fa[2][CH][2];
-      uint4 fb[2][2][2];
-      rd(0, fa[0], fb[0]);
-#pragma unroll
-      for (int step = 0; step < 4; ++step) {
-        if (step + 1 < 4) rd(step + 1, fa[(step + 1) & 1], fb[(step + 1) & 1]);
-        const int cur = step & 1;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int c = 0; c < CH; ++c) {
-            dvacc[kb][c] = mfma32(fa[cur][c][0], as_bf16x8(fb[cur][kb][0]), dvacc[kb][c]);
-            dkacc[kb][c] = mfma32(fa[cur][c][1], as_bf16x8(fb[cur][kb][1]), dkacc[kb][c]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    tile_loop(consume, [](int) {});
 
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int kc = kb0 + 32 * (kp_first + kb) + l32;  // this lane's key in key block kb
-      if (kc < e) {
-        bf16* ko = a.dk + base + (size_t)kc * rs;
-        bf16* vo = a.dv + base + (size_t)kc * rs;
-        if constexpr (kRing) {
-          float* ka = a.dk_acc + base + (size_t)kc * rs;
-          float* va = a.dv_acc + base + (size_t)kc * rs;
-#pragma unroll
-          for (int c = 0; c < CH; ++c)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * (cb0 + c) + 8 * gq + 4 * half;
-              add_store4(ka + col, dkacc[kb][c], 4 * gq, a.scale, rb.first, rb.last ? ko + col : nullptr);
-              add_store4(va + col, dvacc[kb][c], 4 * gq, 1.f, rb.first, rb.last ? vo + col : nullptr);
+    // The tile loop, with the three stages named per iteration (i mod 3):
+    // work(i, cur, prev) runs between the loads of tile i + 1 going out and the
+    // first barrier, publish(i) between the two barriers. Producers and
+    // consumers run it with their own bodies, so that each role's registers are
+    // its own; both pass the same barriers.
+    auto tile_loop = [&](auto work, auto publish) {
+      auto iteration = [&](int i, const KvStage<D>& cur, const KvStage<D>& prev, KvStage<D>& next) {
+        if (i + 1 < ntiles) load_tile(i + 1, next);
+        work(i, cur, prev);
+        barrier_lds_only();  // the consumer has read the P/dS buffer
+        publish(i);
+        wait_vmem();
+        __syncthreads();  // new P/dS and tile i + 1 visible
+      };
+      load_tile(0, st0);
+      wait_vmem();
+      __syncthreads();
+      for (int i = 0; i <= ntiles; i += 3) {
+        iteration(i, st0, st2, st1);
+        if (i + 1 <= ntiles) iteration(i + 1, st1, st0, st2);
+        if (i + 2 <= ntiles) iteration(i + 2, st2, st1, st0);
+      }
+    };
+
+    if constexpr (producer) {
+      // K^T and V^T of the pair's 32 keys (zero past the document end)
+      uint4 kreg[KK], vreg[KK];
+      {
+        const long long span = (long long)(e - kp0) * row_bytes;
+        const rsrc_t kr = make_rsrc(a.k + base + (size_t)kp0 * rs, span);
+        const rsrc_t vr = make_rsrc(a.v + base + (size_t)kp0 * rs, span);
+        const uint32_t off = (uint32_t)l32 * row_bytes + (uint32_t)(8 * half) * 2u;
+  #pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          kreg[kk] = buf_load16(kr, off + 32u * kk);
+          vreg[kk] = buf_load16(vr, off + 32u * kk);
+        }
+      }
+      // P and dS of both query blocks as MFMA B operands: pk[4 qb + mm] = P,
+      // pk[4 qb + 2 + mm] = dS, accumulator elements 8 mm .. 8 mm + 7
+      uint4 pk[8];
+      auto produce = [&](int i, const KvStage<D>& st, const KvStage<D>&) {
+        if (i >= ntiles) return;
+        const int qt0 = qlast - i * kKvBQ;
+        // tiles that cross the diagonal or a document end are masked element by element
+        const bool need_mask = (causal && qt0 < kp0 + 31) || qt0 + kKvBQ > e || kp0 + 32 > e;
+        // S = Q K^T and dP = dO V^T of both 32-query blocks. The exponentials of
+        // block 0 run between the MFMAs of block 1, four elements every other
+        // k-step (their lse2 and D read one step before), so the wave's own
+        // matrix work covers half of its softmax.
+        // dP starts from -D of its queries (the pre-pass stores D negated), so
+        // the MFMAs leave dP - D and the softmax has no subtraction to do
+        f32x16 sacc[2], pacc[2];
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb) {
+  #pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const float4 d4 = *reinterpret_cast<const float4*>(st.dlt + 32 * qb + 8 * gq + 4 * half);
+            sacc[qb][4 * gq] = sacc[qb][4 * gq + 1] = sacc[qb][4 * gq + 2] = sacc[qb][4 * gq + 3] = 0.f;
+            pacc[qb][4 * gq] = d4.x;
+            pacc[qb][4 * gq + 1] = d4.y;
+            pacc[qb][4 * gq + 2] = d4.z;
+            pacc[qb][4 * gq + 3] = d4.w;
+          }
+        }
+        // Q and dO fragments read two k-steps ahead of their MFMAs
+        auto rd = [&](int qb, int kk, uint4* f) {
+          const uint32_t off = fo.row_frag(qb, kk);
+          f[0] = lds_ld16(st.q, off);
+          f[1] = lds_ld16(st.dout, off);
+        };
+        // lse2 of the four queries of accumulator elements 4 gq .. 4 gq + 3
+        auto rd_ld = [&](int qb, int gq, float4& l4) {
+          l4 = *reinterpret_cast<const float4*>(st.lse2 + 32 * qb + 8 * gq + 4 * half);
+        };
+        // in place: sacc becomes P
+        auto soft4 = [&](int qb, int gq, const float4& l4) {
+          const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+  #pragma unroll
+          for (int x = 0; x < 4; ++x) {
+            const int i2 = 4 * gq + x;
+            sacc[qb][i2] = fast_exp2(fmaf(sacc[qb][i2], a.sl2, -lv[x]));
+          }
+        };
+        // masked P (zero where the key is not visible to the query) and P (dP - D)
+        // of accumulator elements 8 mm .. 8 mm + 7 of block qb, packed to bf16
+        auto pack8 = [&](int qb, int mm) {
+          const int b = 8 * mm;
+          if (need_mask) {
+  #pragma unroll
+            for (int x = b; x < b + 8; ++x) {
+              const int qq = qt0 + 32 * qb + 8 * (x >> 2) + 4 * half + (x & 3);
+              if (qq >= e || kj >= e || (causal && kj > qq)) sacc[qb][x] = 0.f;
             }
-        } else {
-#pragma unroll
-          for (int c = 0; c < CH; ++c)
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int col = 32 * (cb0 + c) + 8 * gq + 4 * half;
-              *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[kb][c], 4 * gq, a.scale);
-              *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[kb][c], 4 * gq, 1.f);
+          }
+          const f32x16& p = sacc[qb];
+          const f32x16& ds = pacc[qb];
+          pk[4 * qb + mm] = make_uint4(pack_bf16x2(p[b], p[b + 1]), pack_bf16x2(p[b + 2], p[b + 3]),
+                                       pack_bf16x2(p[b + 4], p[b + 5]), pack_bf16x2(p[b + 6], p[b + 7]));
+          pk[4 * qb + 2 + mm] = make_uint4(pack_bf16x2(p[b] * ds[b], p[b + 1] * ds[b + 1]),
+                                           pack_bf16x2(p[b + 2] * ds[b + 2], p[b + 3] * ds[b + 3]),
+                                           pack_bf16x2(p[b + 4] * ds[b + 4], p[b + 5] * ds[b + 5]),
+                                           pack_bf16x2(p[b + 6] * ds[b + 6], p[b + 7] * ds[b + 7]));
+        };
+        {
+          uint4 fr[3][2];
+          rd(0, 0, fr[0]);
+          rd(0, 1, fr[1]);
+  #pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) rd(0, kk + 2, fr[(kk + 2) % 3]);
+            sacc[0] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[0]);
+            pacc[0] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[0]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+        {
+          uint4 fr[3][2];
+          float4 l4;
+          rd(1, 0, fr[0]);
+          rd(1, 1, fr[1]);
+  #pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            if (kk + 2 < KK) rd(1, kk + 2, fr[(kk + 2) % 3]);
+            if ((kk & 1) == 0 && kk / 2 < 4) rd_ld(0, kk / 2, l4);
+            sacc[1] = mfma32(as_bf16x8(fr[kk % 3][0]), as_bf16x8(kreg[kk]), sacc[1]);
+            pacc[1] = mfma32(as_bf16x8(fr[kk % 3][1]), as_bf16x8(vreg[kk]), pacc[1]);
+            if ((kk & 1) == 1 && kk / 2 < 4) soft4(0, kk / 2, l4);
+            if (kk == 3 || kk == 7) pack8(0, kk / 4);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // with D = 64 there are only four k-steps: the rest of block 0 here
+  #pragma unroll
+          for (int gq = KK / 2; gq < 4; ++gq) {
+            rd_ld(0, gq, l4);
+            soft4(0, gq, l4);
+          }
+          if (KK < 8) pack8(0, 1);
+  #pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            rd_ld(1, gq, l4);
+            soft4(1, gq, l4);
+          }
+        }
+  #pragma unroll
+        for (int mm = 0; mm < 2; ++mm) pack8(1, mm);
+      };
+      auto publish = [&](int i) {
+        if (i >= ntiles) return;
+  #pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) xbuf[((pair * 2 + qb) * 4 + j) * 64 + lane] = pk[4 * qb + j];
+      };
+      tile_loop(produce, publish);
+    } else {
+      // Consumer c takes the P/dS of producer pairs 2 (c/2) and 2 (c/2) + 1 (64
+      // keys) and accumulates dK^T, dV^T for half of the D columns, those of
+      // column blocks CH (c % 2) .. CH (c % 2) + CH - 1: every A fragment (dO^T,
+      // Q^T) it reads serves both key blocks and every P/dS operand both column
+      // blocks.
+      constexpr int CH = CB / 2;
+      const int kp_first = 2 * (pair >> 1);  // first producer pair of this consumer
+      const int cb0 = CH * (pair & 1);
+      f32x16 dkacc[2][CH], dvacc[2][CH];  // [key block][column block]
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+        for (int c = 0; c < CH; ++c)
+  #pragma unroll
+          for (int i = 0; i < 16; ++i) dkacc[kb][c][i] = dvacc[kb][c][i] = 0.f;
+      // the previous tile, in four steps (query block qb, 16-query half hf):
+      // A = dO^T, Q^T of those 16 queries for the CH column blocks, B = P, dS
+      // of the two key blocks; the next step's operands are read while this
+      // step's MFMAs run
+      auto consume = [&](int i, const KvStage<D>&, const KvStage<D>& st) {
+        if (i < 1) return;
+        auto rd = [&](int step, bf16x8 (*fa)[2], uint4 (*fb)[2]) {
+          const int qb = step >> 1, hf = step & 1;
+  #pragma unroll
+          for (int c = 0; c < CH; ++c) {
+            fa[c][0] = a_from_rows_at<D>(st.dout, fo, 2 * qb + hf, cb0 + c);
+            fa[c][1] = a_from_rows_at<D>(st.q, fo, 2 * qb + hf, cb0 + c);
+          }
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) {
+            fb[kb][0] = xbuf[(((kp_first + kb) * 2 + qb) * 4 + hf) * 64 + lane];
+            fb[kb][1] = xbuf[(((kp_first + kb) * 2 + qb) * 4 + 2 + hf) * 64 + lane];
+          }
+        };
+        bf16x8 fa[2][CH][2];
+        uint4 fb[2][2][2];
+        rd(0, fa[0], fb[0]);
+  #pragma unroll
+        for (int step = 0; step < 4; ++step) {
+          if (step + 1 < 4) rd(step + 1, fa[(step + 1) & 1], fb[(step + 1) & 1]);
+          const int cur = step & 1;
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+            for (int c = 0; c < CH; ++c) {
+              dvacc[kb][c] = mfma32(fa[cur][c][0], as_bf16x8(fb[cur][kb][0]), dvacc[kb][c]);
+              dkacc[kb][c] = mfma32(fa[cur][c][1], as_bf16x8(fb[cur][kb][1]), dkacc[kb][c]);
             }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      tile_loop(consume, [](int) {});
+
+  #pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int kc = kb0 + 32 * (kp_first + kb) + l32;  // this lane's key in key block kb
+        if (kc < e) {
+          bf16* ko = a.dk + base + (size_t)kc * rs;
+          bf16* vo = a.dv + base + (size_t)kc * rs;
+          if constexpr (kRing) {
+            float* ka = a.dk_acc + base + (size_t)kc * rs;
+            float* va = a.dv_acc + base + (size_t)kc * rs;
+  #pragma unroll
+            for (int c = 0; c < CH; ++c)
+  #pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int col = 32 * (cb0 + c) + 8 * gq + 4 * half;
+                add_store4(ka + col, dkacc[kb][c], 4 * gq, a.scale, rb.first, rb.last ? ko + col : nullptr);
+                add_store4(va + col, dvacc[kb][c], 4 * gq, 1.f, rb.first, rb.last ? vo + col : nullptr);
+              }
+          } else {
+  #pragma unroll
+            for (int c = 0; c < CH; ++c)
+  #pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                const int col = 32 * (cb0 + c) + 8 * gq + 4 * half;
+                *reinterpret_cast<uint2*>(ko + col) = pack4_scaled(dkacc[kb][c], 4 * gq, a.scale);
+                *reinterpret_cast<uint2*>(vo + col) = pack4_scaled(dvacc[kb][c], 4 * gq, 1.f);
+              }
+          }
         }
       }
     }
+  };
+  TileId t;
+  if (w < 4) {
+    while (tq.next(t, s_claim)) tile(t, RoleTag<true>{});
+  } else {
+    while (tq.next(t, s_claim)) tile(t, RoleTag<false>{});
   }
+  tq.finish();
 }
 
 }  // namespace
 
 namespace uly_host {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+// The queue counters behind the 2 * rows floats of a backward workspace
+// (256-byte aligned offset; ulysses_attn_bwd_workspace_bytes counts them).
+constexpr size_t kSchedBytes = 256;
+inline size_t sched_offset(size_t rows) { return (2 * rows * sizeof(float) + 255) / 256 * 256; }
+int* sched_counters(float* ws, size_t rows) {
+  return reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + sched_offset(rows));
+}
 
 // The tile decode forms nslots * ndoc * max(units, kUnitGroup) in int, for
 // the dQ kernel's 256-query tiles and the dK/dV kernel's 128-key tiles.
@@ -783,6 +843,7 @@ int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const
   a.step = 0;
   a.sp = 1;
   a.B = 1;
+  a.sched = nullptr;
   const int maxlen = g.cu ? g.max_doc_len : g.N;
   hipStream_t st = (hipStream_t)stream;
 
@@ -793,12 +854,24 @@ int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const
   akv.nslots = (maxlen + kKvBK - 1) / kKvBK;
   const long long kvblocks = (long long)akv.nslots * a.ndoc * a.units;
 
+  // Persistent launches: one workgroup per compute unit (each kernel holds a
+  // whole CU), taking tiles from the queues in the workspace's tail, which
+  // the pre-pass cleared and each kernel leaves cleared.
+  const int ncu = device_cu_count();
+  int* sched = sched_counters(const_cast<float*>(delta), (size_t)g.G * g.Hl * g.N);
+  long long kvgrid = kvblocks, qgrid = qblocks;
+  if (ncu > 0) {
+    akv.sched = sched;
+    aq.sched = sched + kSchedDq;
+    kvgrid = kvblocks < ncu ? kvblocks : ncu;
+    qgrid = qblocks < ncu ? qblocks : ncu;
+  }
   if (g.d == 64) {
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<64, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, false>), dim3((unsigned)kvgrid), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<64, false>), dim3((unsigned)qgrid), dim3(kDqThreads), 0, st, aq);
   } else {
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, false>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<128, false>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, false>), dim3((unsigned)kvgrid), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<128, false>), dim3((unsigned)qgrid), dim3(kDqThreads), 0, st, aq);
   }
   return launch_status();
 }
@@ -807,7 +880,7 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* delta, const AttnGeom& g, void* stream) {
   if (!bwd_tiles_fit(g)) return ULY_ESHAPE;  // before the pre-pass is enqueued
-  const int rc = launch_attn_bwd_prepare_bf16(o, dout, lse, delta, g, stream);
+  const int rc = launch_attn_bwd_prepare_bf16(o, dout, lse, delta, g, stream, true);
   if (rc != ULY_OK) return rc;
   return launch_attn_bwd_main_bf16(q, k, v, dout, lse, dq, dk, dv, delta, g, stream);
 }
@@ -815,7 +888,7 @@ int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void
 // The D pre-pass over G rows of N tokens and Hl heads: -D and lse * log2(e)
 // into the workspace (Ulysses shares and ring chunks alike).
 int launch_attn_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
-                                 const AttnGeom& g, void* stream) {
+                                 const AttnGeom& g, void* stream, bool with_sched) {
   const long long rows = (long long)g.G * g.Hl * g.N;
   const long long units = (long long)g.G * g.Hl;
   const int tpb = kDeltaPasses * kThreads / (g.d / 8);  // tokens per block
@@ -823,13 +896,14 @@ int launch_attn_bwd_prepare_bf16(const void* o, const void* dout, const float* l
   const bf16* ob = static_cast<const bf16*>(o);
   const bf16* db = static_cast<const bf16*>(dout);
   float* lse2 = delta + (size_t)rows;
+  int* sched = with_sched ? sched_counters(delta, (size_t)rows) : nullptr;
   hipStream_t st = (hipStream_t)stream;
   if (g.d == 64)
     hipLaunchKernelGGL(delta_bf16_kernel<64>, dgrid, dim3(kThreads), 0, st, ob, db, lse, delta,
-                       lse2, g.N, g.Hl, units);
+                       lse2, g.N, g.Hl, units, sched);
   else
     hipLaunchKernelGGL(delta_bf16_kernel<128>, dgrid, dim3(kThreads), 0, st, ob, db, lse, delta,
-                       lse2, g.N, g.Hl, units);
+                       lse2, g.N, g.Hl, units, sched);
   return launch_status();
 }
 
@@ -862,6 +936,7 @@ int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void
   a.step = step;
   a.sp = sp;
   a.B = B;
+  a.sched = nullptr;  // one tile per workgroup (the ring's workspace has no queue counters)
   BwdArgs aq = a;
   aq.nslots = (g.N + kDqBQ - 1) / kDqBQ;
   BwdArgs akv = a;
@@ -886,8 +961,9 @@ int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void
 extern "C" size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl, int d, int dtype) {
   if (sp <= 0 || B <= 0 || N <= 0 || Hl <= 0) return 0;
   if (!uly_host::dtype_ok(dtype) || !uly_host::head_dim_ok(d)) return 0;
-  // -D = -rowsum(dO * O) and lse in log2 units: two floats per (rank, batch row, head, token).
-  return 2 * (size_t)sp * B * Hl * N * sizeof(float);
+  // -D = -rowsum(dO * O) and lse in log2 units: two floats per (rank, batch row, head, token),
+  // then the tile-queue counters of the dK/dV and dQ kernels.
+  return uly_host::sched_offset((size_t)sp * B * Hl * N) + uly_host::kSchedBytes;
 }
 
 extern "C" int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,
@@ -950,11 +1026,11 @@ extern "C" int ulysses_attn_bwd_prepare(const void* o, const void* dout, const f
   if (dtype == ULY_F32)
     return uly_host::launch_attn_bwd_prepare_f32(static_cast<const float*>(o), static_cast<const float*>(dout),
                                                  delta, g, stream);
-  return uly_host::launch_attn_bwd_prepare_bf16(o, dout, lse, delta, g, stream);
+  return uly_host::launch_attn_bwd_prepare_bf16(o, dout, lse, delta, g, stream, true);
 }
 
 extern "C" int ulysses_attn_bwd_prepared(const void* q, const void* k, const void* v, const void* dout,
-                                         const float* lse, void* dq, void* dk, void* dv, const void* workspace,
+                                         const float* lse, void* dq, void* dk, void* dv, void* workspace,
                                          size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len,
                                          int sp, int B, int N, int Hl, int d, int causal, int dtype, void* stream) {
   if (!q || !k || !v || !dout || !lse || !dq || !dk || !dv) return ULY_EINVAL;

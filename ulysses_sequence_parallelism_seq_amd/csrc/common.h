@@ -276,6 +276,86 @@ __device__ __forceinline__ TileId decode_tile(int bid, int nslots, int ndoc, int
   t.unit = gi * kUnitGroup + (rem - t.doc * ug);
   return t;
 }
+
+// Tiles of a persistent launch (one workgroup per CU, each taking tile after
+// tile until none is left), claimed from eight lists, one per XCD: list x
+// holds the tiles of units u = x (mod 8) in the order of decode_tile
+// (unit-group by unit-group, each in level order: the longest causal work
+// first). A workgroup takes from its own XCD's list while it lasts, so that
+// XCD's L2 keeps serving the few heads it works on, then from the others'
+// lists: XCDs that run at a higher clock take over the work of slower ones
+// instead of idling. Claims are atomic adds on counters in caller memory;
+// each tile is still computed whole by one workgroup, so the results do not
+// depend on the assignment. The last workgroup to finish sets the counters
+// back to zero for the next launch on the same memory.
+// With ctr == nullptr a workgroup handles the one tile blockIdx.x names.
+constexpr int kQueueInts = 9;  // 8 claim counters, then the count of finished workgroups
+struct TileQueue {
+  int* ctr;
+  int nslots, ndoc, units;
+  int x0;         // this workgroup's XCD
+  unsigned live;  // lists not yet found exhausted (thread 0)
+  bool pending;   // one-tile mode: the tile is still to be handed out
+
+  __device__ __forceinline__ void init(int* c, int nslots_, int ndoc_, int units_) {
+    ctr = c;
+    nslots = nslots_;
+    ndoc = ndoc_;
+    units = units_;
+    x0 = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 7;  // HW_REG_XCC_ID
+    live = 0xffu;
+    pending = true;
+  }
+  // tiles in list x
+  __device__ __forceinline__ int list_len(int x) const {
+    const int nu = units / kUnitGroup + (x < units % kUnitGroup ? 1 : 0);
+    return nu * nslots * ndoc;
+  }
+  // The next tile of this workgroup; false when there is none. Workgroup-
+  // uniform; contains barriers in the persistent mode (every thread calls it).
+  __device__ __forceinline__ bool next(TileId& t, int* s_claim) {
+    if (!ctr) {
+      if (!pending) return false;
+      pending = false;
+      t = decode_tile(blockIdx.x, nslots, ndoc, units);
+      return true;
+    }
+    __syncthreads();  // every wave is done with the previous tile and with s_claim
+    if (threadIdx.x == 0) {
+      int cx = -1, ct = 0;
+      for (int k = 0; k < kUnitGroup && cx < 0; ++k) {
+        const int x = (x0 + k) & 7;
+        if (!((live >> x) & 1u)) continue;
+        const int n = list_len(x);
+        const int i = n > 0 ? atomicAdd(&ctr[x], 1) : 0;
+        if (i < n) {
+          cx = x;
+          ct = i;
+        } else {
+          live &= ~(1u << x);
+        }
+      }
+      s_claim[0] = cx;
+      s_claim[1] = ct;
+    }
+    __syncthreads();
+    const int x = s_claim[0], i = s_claim[1];
+    if (x < 0) return false;
+    const int per = nslots * ndoc;
+    const int gi = i / per, r = i - gi * per;
+    t.lvl = r / ndoc;
+    t.doc = r - t.lvl * ndoc;
+    t.unit = gi * kUnitGroup + x;
+    return true;
+  }
+  // After the last next(): counts this workgroup out; the last one resets the counters.
+  __device__ __forceinline__ void finish() {
+    if (!ctr || threadIdx.x != 0) return;
+    if (__hip_atomic_fetch_add(&ctr[8], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
+      for (int x = 0; x < kQueueInts; ++x) __hip_atomic_store(&ctr[x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+};
 }  // namespace uly
 
 // ---------------------------------------------------------------- host side
@@ -285,6 +365,9 @@ namespace uly_host {
 inline bool dtype_ok(int dtype) { return dtype == ULY_F32 || dtype == ULY_BF16; }
 inline bool head_dim_ok(int d) { return d == 64 || d == 128; }
 inline size_t elem_size(int dtype) { return dtype == ULY_F32 ? 4 : 2; }
+
+// Compute units of the current device (the grid of a persistent launch), or 0.
+int device_cu_count();
 
 inline int launch_status() {
   hipError_t e = hipGetLastError();

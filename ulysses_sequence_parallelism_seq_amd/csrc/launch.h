@@ -34,8 +34,10 @@ int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, f
 int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* delta, const AttnGeom& a, void* stream);
+// with_sched: the workspace also holds the persistent kernels' queue
+// counters (ulysses_attn_bwd's layout), which the pre-pass clears.
 int launch_attn_bwd_prepare_bf16(const void* o, const void* dout, const float* lse, float* delta,
-                                 const AttnGeom& a, void* stream);
+                                 const AttnGeom& a, void* stream, bool with_sched);
 int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const void* dout,
                               const float* lse, void* dq, void* dk, void* dv, const float* delta,
                               const AttnGeom& a, void* stream);

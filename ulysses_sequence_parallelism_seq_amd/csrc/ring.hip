@@ -70,7 +70,7 @@ extern "C" int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, co
   if (!workspace || workspace_bytes < ulysses_ring_attn_bwd_workspace_bytes(sp, B, Ns, H, d, dtype))
     return ULY_EWORKSPACE;
   return uly_host::launch_attn_bwd_prepare_bf16(o, dout, lse, static_cast<float*>(workspace),
-                                                ring_geom(sp, B, Ns, H, d, 1), stream);
+                                                ring_geom(sp, B, Ns, H, d, 1), stream, false);
 }
 
 extern "C" int ulysses_ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* dout,
