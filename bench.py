@@ -97,6 +97,7 @@ def make_buffers(w: workloads.Workload, dev):
                      torch.empty((w.sp, w.B, w.Hl, w.N), dtype=torch.float32, device=dev)]
                     + [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(3)],
         "seq_out": [torch.empty_like(seq_in[0]) for _ in range(4)],
+        "fws": torch.empty(uly.ulysses_attn_fwd_workspace_bytes(), dtype=torch.uint8, device=dev),
         "ws": torch.empty(uly.ulysses_attn_bwd_workspace_bytes(w.sp, w.B, w.N, w.Hl, w.d, dt),
                           dtype=torch.uint8, device=dev),
     }
@@ -136,7 +137,8 @@ def step(w, bufs, packing, timer=None):
     run("seq_to_head", lambda: uly.ulysses_seq_to_head(qs, out=qh))
     run("seq_to_head", lambda: uly.ulysses_seq_to_head(ks, out=kh))
     run("seq_to_head", lambda: uly.ulysses_seq_to_head(vs, out=vh))
-    run("attn_fwd", lambda: uly.ulysses_attn_fwd(qh, kh, vh, packing, w.causal, out=o, lse=lse))
+    run("attn_fwd", lambda: uly.ulysses_attn_fwd(qh, kh, vh, packing, w.causal, out=o, lse=lse,
+                                                 workspace=bufs["fws"]))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(o, out=os_))
     run("seq_to_head", lambda: uly.ulysses_seq_to_head(dos, out=doh))
     # ulysses_attn_bwd in its two steps, timed apart: the D pre-pass, then the dK/dV and dQ kernels

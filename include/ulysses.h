@@ -119,6 +119,29 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float
                      int Hl, int d, int causal, int dtype, void* stream);
 
 /*
+ * ulysses_attn_fwd with a persistent launch, for callers that can lend it
+ * ulysses_attn_fwd_workspace_bytes() (256) bytes of device memory: one
+ * workgroup per compute unit takes the 256-query tiles from eight queues,
+ * one per XCD (an XCD's own heads first, so its L2 keeps serving them, then
+ * the other XCDs' remaining tiles), instead of the hardware's fixed
+ * round-robin of one workgroup per tile. XCDs that run at a higher clock
+ * then take over work of the slower ones, empty tiles of short documents
+ * cost no dispatch, and no workgroup waits to be launched. Same arguments,
+ * results (bit for bit: every tile is still computed whole by one
+ * workgroup) and errors as ulysses_attn_fwd, plus
+ *   workspace        device memory, >= ulysses_attn_fwd_workspace_bytes()
+ *                    bytes, 4-byte aligned; contents on entry ignored (a
+ *                    small kernel on the stream clears the counters first),
+ *                    left zeroed. Calls that overlap in time need their own.
+ * Errors: as ulysses_attn_fwd; ULY_EWORKSPACE (workspace NULL or too small).
+ * The fp32 path ignores the workspace.
+ */
+size_t ulysses_attn_fwd_workspace_bytes(void);
+int ulysses_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                        size_t workspace_bytes, const int* cu_seqlens, int ndoc, int max_doc_len, int sp, int B,
+                        int N, int Hl, int d, int causal, int dtype, void* stream);
+
+/*
  * Bytes of device workspace ulysses_attn_bwd needs: two floats per (rank,
  * batch row, head, token) (the row sums D = rowsum(dO * O), stored negated,
  * and lse in log2 units), i.e. O(N), never O(N^2), rounded up to 256 bytes,

@@ -29,6 +29,7 @@ def test_library_exports_every_declared_function():
     names = declared_functions()
     assert set(names) == {
         "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
+        "ulysses_attn_fwd_ws", "ulysses_attn_fwd_workspace_bytes",
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_attn_bwd_noalloc",
         "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
         "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
@@ -74,6 +75,14 @@ def test_attention_argument_errors():
                    a["Hl"], a["d"], a["causal"], a["dtype"], None)
 
     assert fwd(None, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
+    # the persistent forward: 256 bytes of queue counters, else ULY_EWORKSPACE; then the same checks
+    fws = lib.ulysses_attn_fwd_ws
+    assert lib.ulysses_attn_fwd_workspace_bytes() == 256
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, None, 256, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 255, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert fws(None, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None, 1, 8, 1, 1, 8, 2, 48, 1, 1, None) == EUNSUP
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 1, 9, 1, 1, 8, 2, 64, 1, 1, None) == ESHAPE
     assert call(N=0) == EINVAL
     assert call(d=32) == EUNSUP
     assert call(dtype=3) == EUNSUP

@@ -230,6 +230,43 @@ def test_backward_in_two_calls_equals_one(dtype, d):
         assert torch.equal(a, b), name
 
 
+@pytest.mark.parametrize("shape,lengths,causal", [
+    ((4, 2, 4096, 8, 128), None, True),                     # the llama7b workload's shares (full size)
+    ((1, 1, 3000, 8, 128), [900, 0, 1, 1200, 899], True),   # empty and one-token documents
+    ((3, 1, 1000, 3, 64), [1, 999], False),
+])
+def test_persistent_launch_equals_one_tile_per_workgroup(shape, lengths, causal):
+    """The persistent launches (ulysses_attn_fwd_ws; the backward's dK/dV and dQ
+    kernels) compute every tile whole in one workgroup: the same bits as the
+    one-tile-per-workgroup forward, whatever the workspace held on entry, and
+    one prepare serves several prepared calls (each kernel leaves its queue
+    counters cleared)."""
+    say("persistent == one tile per workgroup", shape, lengths, causal)
+    dev = device()
+    sp, B, N, Hl, d = shape
+    packing = None if lengths is None else uly.DocPacking(workloads.cu_seqlens_from_lengths(lengths), N, dev)
+    q, k, v, do = (t.to(dev) for t in workloads.qkv_do(shape, 43, "bf16"))
+    o1, lse1 = uly.ulysses_attn_fwd(q, k, v, packing, causal, persistent=False)
+    fws = torch.full((uly.ulysses_attn_fwd_workspace_bytes(),), 0xFF, dtype=torch.uint8, device=dev)
+    o2, lse2 = uly.ulysses_attn_fwd(q, k, v, packing, causal, workspace=fws)
+    o3, lse3 = uly.ulysses_attn_fwd(q, k, v, packing, causal, workspace=fws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(lse1, lse2), "forward, dirty workspace"
+    assert torch.equal(o1, o3) and torch.equal(lse1, lse3), "forward, workspace reused"
+    # the queue counters (nine ints at the workspace's start) are left cleared; the rest is untouched
+    assert torch.count_nonzero(fws[:36]).item() == 0, "the forward leaves its counters cleared"
+    assert torch.all(fws[36:] == 0xFF).item(), "the forward writes only its counters"
+    ws = torch.full((uly.ulysses_attn_bwd_workspace_bytes(*shape, torch.bfloat16),), 0xFF, dtype=torch.uint8,
+                    device=dev)
+    g1 = uly.ulysses_attn_bwd(q, k, v, o1, do, lse1, packing, causal, workspace=ws)
+    uly.ulysses_attn_bwd_prepare(o1, do, lse1, ws)
+    g2 = uly.ulysses_attn_bwd_prepared(q, k, v, do, lse1, ws, packing, causal)
+    g3 = uly.ulysses_attn_bwd_prepared(q, k, v, do, lse1, ws, packing, causal)
+    torch.cuda.synchronize()
+    for name, a, b, c in zip(("dq", "dk", "dv"), g1, g2, g3):
+        assert torch.equal(a, b) and torch.equal(a, c), name
+
+
 def test_bf16_bitwise_reproducible():
     say("bf16 reproducible")
     q, k, v, do = workloads.qkv_do((1, 1, 1500, 2, 128), 5, "bf16")

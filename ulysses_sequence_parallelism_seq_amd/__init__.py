@@ -10,7 +10,9 @@ missing library is an error.
 Functions carry the C names:
   ulysses_seq_to_head(x_seq, sp)          [sp,B,N/sp,H,d] -> [sp,B,N,H/sp,d]
   ulysses_head_to_seq(x_head, sp)         [sp,B,N,H/sp,d] -> [sp,B,N/sp,H,d]
-  ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)
+  ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)  (bf16: the persistent launch of
+                                          ulysses_attn_fwd_ws unless persistent=False)
+  ulysses_attn_fwd_workspace_bytes()
   ulysses_attn_bwd(q, k, v, o, dout, lse, ...) -> (dq, dk, dv)
   ulysses_attn_bwd_workspace_bytes(...), ulysses_status_string(code)
   ulysses_attn_bwd_prepare(o, dout, lse, workspace)  the D pre-pass alone
@@ -65,6 +67,9 @@ def library() -> ctypes.CDLL:
         lib.ulysses_seq_to_head.argtypes = [vp, vp, i, i, i, i, i, i, vp]
         lib.ulysses_head_to_seq.argtypes = [vp, vp, i, i, i, i, i, i, vp]
         lib.ulysses_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
+        lib.ulysses_attn_fwd_workspace_bytes.argtypes = []
+        lib.ulysses_attn_fwd_workspace_bytes.restype = sz
+        lib.ulysses_attn_fwd_ws.argtypes = [vp] * 6 + [sz, vp] + [i] * 9 + [vp]
         lib.ulysses_attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
         lib.ulysses_attn_bwd_workspace_bytes.restype = sz
         lib.ulysses_attn_bwd.argtypes = [vp] * 10 + [sz, vp] + [i] * 9 + [vp]
@@ -85,7 +90,8 @@ def library() -> ctypes.CDLL:
         lib.ulysses_tiled_mlp_bwd.argtypes = [vp] * 10 + [sz] + [i] * 4 + [vp]
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
-        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
+        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_fwd_ws",
+                     "ulysses_attn_bwd",
                      "ulysses_attn_bwd_noalloc", "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
                      "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
                      "ulysses_sp_loss", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd"):
@@ -189,11 +195,16 @@ def _share_shape(q: torch.Tensor):
     raise ValueError("q must be [B, N, Hl, d] or [sp, B, N, Hl, d]")
 
 
-def ulysses_attn_fwd(q, k, v, cu_seqlens=None, causal: bool = True, out=None, lse=None):
+def ulysses_attn_fwd(q, k, v, cu_seqlens=None, causal: bool = True, out=None, lse=None, workspace=None,
+                     persistent: bool = True):
     """Attention forward over head-sharded shares; returns (o, lse).
 
     q, k, v: [sp, B, N, Hl, d] or [B, N, Hl, d]; lse is [..., Hl, N] float32.
     cu_seqlens: None, host int sequence / tensor, or a DocPacking.
+    persistent (bf16): the persistent launch of ulysses_attn_fwd_ws, with
+    `workspace` (>= ulysses_attn_fwd_workspace_bytes() bytes on the device;
+    allocated here when None); False: ulysses_attn_fwd, one tile per
+    workgroup. Both give the same bits.
     """
     sp, B, N, Hl, d = _share_shape(q)
     for t in (k, v):
@@ -207,10 +218,25 @@ def ulysses_attn_fwd(q, k, v, cu_seqlens=None, causal: bool = True, out=None, ls
     _expect(lse, tuple(q.shape[:-3]) + (Hl, N), torch.float32, "lse")
     _require_device(q, k, v, out, lse)
     cu_dev, ndoc, maxlen = _packing(cu_seqlens, N, q.device)
-    _check("ulysses_attn_fwd", library().ulysses_attn_fwd(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_dev), ndoc, maxlen,
-        sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
+    lib = library()
+    if persistent:
+        need = int(lib.ulysses_attn_fwd_workspace_bytes())
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _require_device(workspace)
+        _check("ulysses_attn_fwd_ws", lib.ulysses_attn_fwd_ws(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _ptr(cu_dev), ndoc, maxlen,
+            sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
+    else:
+        _check("ulysses_attn_fwd", lib.ulysses_attn_fwd(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_dev), ndoc, maxlen,
+            sp, B, N, Hl, d, int(bool(causal)), _dtype_code(q), _stream(q)))
     return out, lse
+
+
+def ulysses_attn_fwd_workspace_bytes() -> int:
+    return int(library().ulysses_attn_fwd_workspace_bytes())
 
 
 def ulysses_attn_bwd_workspace_bytes(sp: int, B: int, N: int, Hl: int, d: int, dtype: torch.dtype) -> int:
@@ -512,6 +538,7 @@ __all__ = [
     "ulysses_seq_to_head",
     "ulysses_head_to_seq",
     "ulysses_attn_fwd",
+    "ulysses_attn_fwd_workspace_bytes",
     "ulysses_attn_bwd",
     "ulysses_attn_bwd_workspace_bytes",
     "ulysses_attn_bwd_noalloc",

@@ -29,8 +29,9 @@ int launch_attn_bwd_main_f32(const float* q, const float* k, const float* v, con
                              const float* lse, float* dq, float* dk, float* dv, const float* delta,
                              const AttnGeom& a, void* stream);
 
+// sched: kQueueInts ints of caller memory for a persistent launch, or nullptr
 int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                         const AttnGeom& a, void* stream);
+                         const AttnGeom& a, void* stream, int* sched);
 int launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, void* dq, void* dk, void* dv,
                          float* delta, const AttnGeom& a, void* stream);
