@@ -279,17 +279,21 @@ __device__ __forceinline__ TileId decode_tile(int bid, int nslots, int ndoc, int
 
 // Tiles of a persistent launch (one workgroup per CU, each taking tile after
 // tile until none is left), claimed from eight lists, one per XCD: list x
-// holds the tiles of units u = x (mod 8) in the order of decode_tile
-// (unit-group by unit-group, each in level order: the longest causal work
-// first). A workgroup takes from its own XCD's list while it lasts, so that
-// XCD's L2 keeps serving the few heads it works on, then from the others'
-// lists: XCDs that run at a higher clock take over the work of slower ones
-// instead of idling. Claims are atomic adds on counters in caller memory;
+// holds the tiles of units u = x (mod 8), in four level groups (the longest
+// causal work first: levels are ordered by decreasing work), each group unit
+// by unit, each unit's part in level order, then document order. Within a
+// group the XCD keeps to one unit (head) at a time, so its L2 serves that
+// head's tiles to all its workgroups; across groups every unit's longest
+// tiles come before any unit's shortest ones, so the list ends with short
+// tiles even when an XCD has few tiles per workgroup. A workgroup takes from
+// its own XCD's list while it lasts, then from the others' lists: XCDs that
+// run at a higher clock take over the work of slower ones instead of idling. Claims are atomic adds on counters in caller memory;
 // each tile is still computed whole by one workgroup, so the results do not
 // depend on the assignment. The last workgroup to finish sets the counters
 // back to zero for the next launch on the same memory.
 // With ctr == nullptr a workgroup handles the one tile blockIdx.x names.
 constexpr int kQueueInts = 9;  // 8 claim counters, then the count of finished workgroups
+constexpr int kLevelGroups = 4;
 struct TileQueue {
   int* ctr;
   int nslots, ndoc, units;
@@ -339,14 +343,26 @@ struct TileQueue {
       s_claim[1] = ct;
     }
     __syncthreads();
-    const int x = s_claim[0], i = s_claim[1];
+    const int x = s_claim[0];
+    int i = s_claim[1];
     if (x < 0) return false;
-    const int per = nslots * ndoc;
-    const int gi = i / per, r = i - gi * per;
-    t.lvl = r / ndoc;
-    t.doc = r - t.lvl * ndoc;
-    t.unit = gi * kUnitGroup + x;
-    return true;
+    const int nu = units / kUnitGroup + (x < units % kUnitGroup ? 1 : 0);
+    const int lg = (nslots + kLevelGroups - 1) / kLevelGroups;  // levels per group
+    int lvl0 = 0;
+    for (int grp = 0; grp < kLevelGroups; ++grp) {
+      const int nl = min(lg, nslots - lvl0);  // levels of this group (the last may hold fewer)
+      const int chunk = nl * ndoc;            // tiles of one unit in this group
+      if (i < nu * chunk) {  // (an empty group, nl = 0, holds no tile)
+        const int ui = i / chunk, r = i - ui * chunk;
+        t.lvl = lvl0 + r / ndoc;
+        t.doc = r - (r / ndoc) * ndoc;
+        t.unit = ui * kUnitGroup + x;
+        return true;
+      }
+      i -= nu * chunk;
+      lvl0 += nl;
+    }
+    return false;
   }
   // After the last next(): counts this workgroup out; the last one resets the counters.
   __device__ __forceinline__ void finish() {
