@@ -1,0 +1,52 @@
+// Host-side check of the persistent launches' tile lists (queue_decode in
+// csrc/common.h): for many geometries, the eight XCD lists together hand out
+// every (unit, level, document) tile exactly once, list x only units
+// u = x (mod 8); within a list the level groups come in order (every tile of
+// group g before any of group g + 1) and, within a group, a unit's tiles are
+// contiguous and in level order. Built for the host only and run by
+// tests/test_tile_queue_cpu.py.
+#include <cstdio>
+#include <set>
+#include <tuple>
+
+#include "common.h"
+
+using namespace uly;
+
+int main() {
+  int bad = 0, cases = 0;
+  const int units_v[] = {1, 2, 3, 7, 8, 9, 13, 16, 32, 64, 65};
+  const int nslots_v[] = {1, 2, 3, 4, 5, 7, 16, 33, 512};
+  const int ndoc_v[] = {1, 2, 4, 13};
+  for (int units : units_v)
+    for (int nslots : nslots_v)
+      for (int ndoc : ndoc_v) {
+        ++cases;
+        std::set<std::tuple<int, int, int>> seen;
+        const int lg = (nslots + kLevelGroups - 1) / kLevelGroups;
+        for (int x = 0; x < kUnitGroup; ++x) {
+          const int n = queue_list_len(x, units, nslots, ndoc);
+          int prev_grp = -1, prev_unit = -1, prev_lvl = -1;
+          std::set<std::pair<int, int>> units_done;  // (group, unit) finished
+          for (int i = 0; i < n; ++i) {
+            const TileId t = queue_decode(x, i, units, nslots, ndoc);
+            const int grp = t.lvl / lg;
+            if (t.unit < 0 || t.unit >= units || t.unit % kUnitGroup != x) ++bad;
+            if (t.lvl < 0 || t.lvl >= nslots || t.doc < 0 || t.doc >= ndoc) ++bad;
+            if (!seen.insert({t.unit, t.lvl, t.doc}).second) ++bad;
+            if (grp < prev_grp) ++bad;  // groups in order
+            if (grp == prev_grp && t.unit != prev_unit) {
+              if (units_done.count({grp, t.unit})) ++bad;  // a unit's part is contiguous
+              units_done.insert({grp, prev_unit});
+            }
+            if (grp == prev_grp && t.unit == prev_unit && t.lvl < prev_lvl) ++bad;  // level order
+            prev_grp = grp;
+            prev_unit = t.unit;
+            prev_lvl = t.lvl;
+          }
+        }
+        if ((int)seen.size() != units * nslots * ndoc) ++bad;
+      }
+  std::printf("tile queue geometries %d, mismatches %d\n", cases, bad);
+  return bad != 0;
+}

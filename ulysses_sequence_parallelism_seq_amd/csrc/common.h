@@ -294,6 +294,34 @@ __device__ __forceinline__ TileId decode_tile(int bid, int nslots, int ndoc, int
 // With ctr == nullptr a workgroup handles the one tile blockIdx.x names.
 constexpr int kQueueInts = 9;  // 8 claim counters, then the count of finished workgroups
 constexpr int kLevelGroups = 4;
+
+// Tiles in the list of XCD x (the units u = x mod 8 of `units`).
+__host__ __device__ __forceinline__ int queue_list_len(int x, int units, int nslots, int ndoc) {
+  const int nu = units / kUnitGroup + (x < units % kUnitGroup ? 1 : 0);
+  return nu * nslots * ndoc;
+}
+// Tile i of the list of XCD x: kLevelGroups groups of lg levels (the last one
+// holds the nslots % lg left over), each group unit by unit, each unit's part
+// level by level, then document by document. Needs i < queue_list_len(...).
+__host__ __device__ __forceinline__ TileId queue_decode(int x, int i, int units, int nslots, int ndoc) {
+  const int nu = units / kUnitGroup + (x < units % kUnitGroup ? 1 : 0);
+  const int lg = (nslots + kLevelGroups - 1) / kLevelGroups;
+  const int full = nslots / lg;      // groups of lg levels
+  const int gsize = nu * lg * ndoc;  // tiles of one such group
+  int grp = i / gsize, nl = lg;
+  if (grp >= full) {                 // the last, shorter group
+    grp = full;
+    nl = nslots - full * lg;
+  }
+  const int r = i - grp * gsize;     // within the group: unit, then level and document
+  const int ui = r / (nl * ndoc), rr = r - ui * (nl * ndoc);
+  TileId t;
+  t.lvl = grp * lg + rr / ndoc;
+  t.doc = rr - (rr / ndoc) * ndoc;
+  t.unit = ui * kUnitGroup + x;
+  return t;
+}
+
 struct TileQueue {
   int* ctr;
   int nslots, ndoc, units;
@@ -310,11 +338,7 @@ struct TileQueue {
     live = 0xffu;
     pending = true;
   }
-  // tiles in list x
-  __device__ __forceinline__ int list_len(int x) const {
-    const int nu = units / kUnitGroup + (x < units % kUnitGroup ? 1 : 0);
-    return nu * nslots * ndoc;
-  }
+  __device__ __forceinline__ int list_len(int x) const { return queue_list_len(x, units, nslots, ndoc); }
   // The next tile of this workgroup; false when there is none. Workgroup-
   // uniform; contains barriers in the persistent mode (every thread calls it).
   __device__ __forceinline__ bool next(TileId& t, int* s_claim) {
@@ -343,26 +367,10 @@ struct TileQueue {
       s_claim[1] = ct;
     }
     __syncthreads();
-    const int x = s_claim[0];
-    int i = s_claim[1];
+    const int x = s_claim[0], i = s_claim[1];
     if (x < 0) return false;
-    const int nu = units / kUnitGroup + (x < units % kUnitGroup ? 1 : 0);
-    const int lg = (nslots + kLevelGroups - 1) / kLevelGroups;  // levels per group
-    int lvl0 = 0;
-    for (int grp = 0; grp < kLevelGroups; ++grp) {
-      const int nl = min(lg, nslots - lvl0);  // levels of this group (the last may hold fewer)
-      const int chunk = nl * ndoc;            // tiles of one unit in this group
-      if (i < nu * chunk) {  // (an empty group, nl = 0, holds no tile)
-        const int ui = i / chunk, r = i - ui * chunk;
-        t.lvl = lvl0 + r / ndoc;
-        t.doc = r - (r / ndoc) * ndoc;
-        t.unit = ui * kUnitGroup + x;
-        return true;
-      }
-      i -= nu * chunk;
-      lvl0 += nl;
-    }
-    return false;
+    t = queue_decode(x, i, units, nslots, ndoc);
+    return true;
   }
   // After the last next(): counts this workgroup out; the last one resets the counters.
   __device__ __forceinline__ void finish() {
