@@ -8,8 +8,10 @@ workload, B=1, N=131072, H=32, sp=8, d=128, bf16, causal):
   head_to_seq(o), seq_to_head(dO)
   attn_bwd over the 8 shares         D pre-pass, then dK/dV + dQ kernels (two calls)
   head_to_seq(dq), (dk), (dv)
-Inputs are seeded synthetic tensors already resident in HBM. Every call is
-timed with HIP events on the stream it runs on.
+Inputs are seeded synthetic tensors already resident in HBM. The timed steps
+(wall clock between two device synchronisations) carry HIP events around the
+backward call alone, the roofline's kernel; a second pass of as many steps
+times every call with HIP events on the stream it runs on.
 
 value = causal attention FLOPs counted as 14 * d * pairs (4 d forward, 10 d
 backward; pairs = sum over documents of L (L + 1) / 2 per row and head)
@@ -104,13 +106,16 @@ def make_buffers(w: workloads.Workload, dev):
 
 
 class Timer:
-    """HIP-event timing of each named call over the timed steps (per-call median)."""
+    """HIP-event timing of each named call (per-call median); with `only`, of those names alone."""
 
-    def __init__(self, stream):
+    def __init__(self, stream, only=None):
         self.stream = stream
+        self.only = only
         self.pending = []
 
     def run(self, name, fn):
+        if self.only is not None and name not in self.only:
+            return fn()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record(self.stream)
@@ -127,6 +132,29 @@ class Timer:
         return {k: statistics.median(v) for k, v in acc.items()}, {k: len(v) for k, v in acc.items()}
 
 
+def timed_steps(one_step, steps, stream, live):
+    """Wall time (s) of `steps` steps between two device synchronisations, with HIP events only
+    around the calls named in `live` (the roofline's kernel), and their medians; then the per-call
+    medians of a second pass of as many steps with events around every call. (An event pair
+    adds a gap of a few microseconds: around all 13 calls, 7% of a 1.5 ms llama7b step.)"""
+    live_timer = Timer(stream, only=set(live))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        one_step(live_timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    timer = Timer(stream)
+    for _ in range(steps):
+        one_step(timer)
+    torch.cuda.synchronize()
+    avg, counts = timer.averages()
+    live_avg, live_counts = live_timer.averages()
+    avg.update(live_avg)
+    counts.update(live_counts)
+    return elapsed, avg, counts
+
+
 def step(w, bufs, packing, timer=None):
     run = timer.run if timer else (lambda name, fn: fn())
     qs, ks, vs, dos = bufs["seq_in"]
@@ -141,10 +169,12 @@ def step(w, bufs, packing, timer=None):
                                                  workspace=bufs["fws"]))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(o, out=os_))
     run("seq_to_head", lambda: uly.ulysses_seq_to_head(dos, out=doh))
-    # ulysses_attn_bwd in its two steps, timed apart: the D pre-pass, then the dK/dV and dQ kernels
-    run("attn_bwd_prepare", lambda: uly.ulysses_attn_bwd_prepare(o, doh, lse, ws))
-    run("attn_bwd_prepared", lambda: uly.ulysses_attn_bwd_prepared(qh, kh, vh, doh, lse, ws, packing, w.causal,
-                                                                   dq=dq, dk=dk, dv=dv))
+
+    def bwd():  # ulysses_attn_bwd in its two steps: the D pre-pass, then the dK/dV and dQ kernels
+        run("attn_bwd_prepare", lambda: uly.ulysses_attn_bwd_prepare(o, doh, lse, ws))
+        run("attn_bwd_prepared", lambda: uly.ulysses_attn_bwd_prepared(qh, kh, vh, doh, lse, ws, packing,
+                                                                       w.causal, dq=dq, dk=dk, dv=dv))
+    run("attn_bwd", bwd)
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dq, out=dqs))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dk, out=dks))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(dv, out=dvs))
@@ -293,16 +323,8 @@ def main():
         step(w, bufs, packing)
     torch.cuda.synchronize()
 
-    timer = Timer(stream)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(w, bufs, packing, timer)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    avg, counts = timer.averages()
-    # the backward = its D pre-pass + the dK/dV and dQ kernels, each timed on its own
-    avg["attn_bwd"] = avg["attn_bwd_prepare"] + avg["attn_bwd_prepared"]
+    elapsed, avg, counts = timed_steps(lambda timer: step(w, bufs, packing, timer), args.steps, stream,
+                                       live=("attn_bwd",))
 
     # reference for the permute: a plain device-to-device copy of one tensor of the same size
     copy_dst = torch.empty_like(seq_in[0])
@@ -351,7 +373,7 @@ def main():
             # the D pre-pass reads O and dO (2 d esize per row) and lse, writes -D and lse2 (8 bytes)
             "attn_bwd_prepare_gbs": round(w.sp * w.B * w.Hl * w.N * (2 * w.d * esize + 12)
                                           / (avg["attn_bwd_prepare"] * 1e-3) / 1e9, 1),
-            "timing": f"HIP events on the launch stream, per-call medians over {args.steps} steps",
+            "timing": f"value: wall clock of {args.steps} steps with HIP events around attn_bwd only (its time: their median); other per-call times: HIP events around every call on the launch stream, medians over {args.steps} more steps",
             "attn_fwd_tflops": round(fwd_tflops, 1),
             "attn_bwd_tflops": round(bwd_tflops, 1),
             "attn_only_tflops": round(flops_step / (attn_ms * 1e-3) / 1e12, 1),
@@ -482,13 +504,7 @@ def mlp_main(args, w, dev):
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    timer = Timer(stream)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        one_step(timer)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    avg, counts = timer.averages()
+    elapsed, avg, counts = timed_steps(one_step, args.steps, stream, live=("mlp_bwd",))
     ms_per_step = elapsed * 1e3 / args.steps
     hi = h * inter * tokens
     flops_step = 22 * hi
@@ -586,13 +602,8 @@ def ring_main(args, w, dev):
     for _ in range(args.warmup):
         ring_step(w, bufs)
     torch.cuda.synchronize()
-    timer = Timer(stream)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        ring_step(w, bufs, timer)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    avg, counts = timer.averages()
+    elapsed, avg, counts = timed_steps(lambda timer: ring_step(w, bufs, timer), args.steps, stream,
+                                       live=("ring_bwd_prepare", "ring_bwd_step"))
     ms_per_step = elapsed * 1e3 / args.steps
     pairs = causal_pairs(w) * w.B * w.H  # the whole sequence, every head
     flops_step = 14 * w.d * pairs

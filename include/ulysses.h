@@ -120,7 +120,7 @@ int ulysses_attn_fwd(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * ulysses_attn_fwd with a persistent launch, for callers that can lend it
- * ulysses_attn_fwd_workspace_bytes() (256) bytes of device memory: one
+ * ulysses_attn_fwd_workspace_bytes() (1152) bytes of device memory: one
  * workgroup per compute unit takes the 256-query tiles from eight queues,
  * one per XCD (an XCD's own heads first, so its L2 keeps serving them, then
  * the other XCDs' remaining tiles), instead of the hardware's fixed
@@ -145,7 +145,7 @@ int ulysses_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, fl
  * Bytes of device workspace ulysses_attn_bwd needs: two floats per (rank,
  * batch row, head, token) (the row sums D = rowsum(dO * O), stored negated,
  * and lse in log2 units), i.e. O(N), never O(N^2), rounded up to 256 bytes,
- * plus 256 bytes of tile-queue counters for the bf16 kernels (they run one
+ * plus 2304 bytes of tile-queue counters for the bf16 kernels (they run one
  * workgroup per compute unit, each taking tiles until none is left; the
  * pre-pass clears the counters and every kernel leaves them cleared).
  * Returns 0 for invalid arguments.
@@ -218,7 +218,7 @@ int ulysses_attn_bwd_prepared(const void* q, const void* k, const void* v, const
  * scratch than the limit; ULY_EHIP when the scratch's device address cannot
  * be looked up.
  */
-#define ULY_NOALLOC_SCRATCH_BYTES (((size_t)64 << 20) + 256)
+#define ULY_NOALLOC_SCRATCH_BYTES (((size_t)64 << 20) + 2304)
 int ulysses_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
                              const float* lse, void* dq, void* dk, void* dv, const int* cu_seqlens, int ndoc,
                              int max_doc_len, int sp, int B, int N, int Hl, int d, int causal, int dtype,

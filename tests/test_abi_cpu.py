@@ -75,14 +75,15 @@ def test_attention_argument_errors():
                    a["Hl"], a["d"], a["causal"], a["dtype"], None)
 
     assert fwd(None, FAKE, FAKE, FAKE, FAKE, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
-    # the persistent forward: 256 bytes of queue counters, else ULY_EWORKSPACE; then the same checks
+    # the persistent forward: 1152 bytes of queue counters (nine on 128-byte lines), else
+    # ULY_EWORKSPACE; then the same checks
     fws = lib.ulysses_attn_fwd_ws
-    assert lib.ulysses_attn_fwd_workspace_bytes() == 256
-    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, None, 256, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
-    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 255, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
-    assert fws(None, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
-    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, None, 1, 8, 1, 1, 8, 2, 48, 1, 1, None) == EUNSUP
-    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 256, FAKE, 1, 9, 1, 1, 8, 2, 64, 1, 1, None) == ESHAPE
+    assert lib.ulysses_attn_fwd_workspace_bytes() == 1152
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, None, 1152, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1151, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert fws(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1152, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EINVAL
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1152, None, 1, 8, 1, 1, 8, 2, 48, 1, 1, None) == EUNSUP
+    assert fws(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1152, FAKE, 1, 9, 1, 1, 8, 2, 64, 1, 1, None) == ESHAPE
     assert call(N=0) == EINVAL
     assert call(d=32) == EUNSUP
     assert call(dtype=3) == EUNSUP
@@ -92,8 +93,8 @@ def test_attention_argument_errors():
     bwd = lib.ulysses_attn_bwd
     need = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 64, 1)
     # D and lse in log2 units, one float each per (unit, token), rounded up to 256 bytes,
-    # then 256 bytes of tile-queue counters
-    assert need == (2 * 1 * 1 * 2 * 8 * 4 + 255) // 256 * 256 + 256
+    # then 2304 bytes of tile-queue counters (two queues)
+    assert need == (2 * 1 * 1 * 2 * 8 * 4 + 255) // 256 * 256 + 2304
     assert lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8, 2, 48, 1) == 0
     ptrs = [FAKE] * 9
     assert bwd(*ptrs, FAKE, need - 1, None, 1, 8, 1, 1, 8, 2, 64, 1, 1, None) == EWS
@@ -121,17 +122,17 @@ def test_noalloc_scratch_size_matches_header():
     assert m, "ULY_NOALLOC_SCRATCH_BYTES not found in the header"
     assert (int(m.group(1)) << int(m.group(2))) + int(m.group(3)) == uly.ULY_NOALLOC_SCRATCH_BYTES
     # the limit in rows stated in the header: two floats per (token, head) row, plus the
-    # 256 bytes of tile-queue counters
-    assert (uly.ULY_NOALLOC_SCRATCH_BYTES - 256) // 8 == 8388608
+    # 2304 bytes of tile-queue counters
+    assert (uly.ULY_NOALLOC_SCRATCH_BYTES - 2304) // 8 == 8388608
     lib = uly.library()
     assert lib.ulysses_attn_bwd_workspace_bytes(1, 1, 8388608, 1, 64, 1) == uly.ULY_NOALLOC_SCRATCH_BYTES
 
 
 def test_workspace_is_linear_in_n():
-    """O(N) workspace: two floats per (unit, token) plus a fixed 256 bytes of queue counters."""
+    """O(N) workspace: two floats per (unit, token) plus a fixed 2304 bytes of queue counters."""
     lib = uly.library()
-    w1 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 131072, 4, 128, 1) - 256
-    w2 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 262144, 4, 128, 1) - 256
+    w1 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 131072, 4, 128, 1) - 2304
+    w2 = lib.ulysses_attn_bwd_workspace_bytes(1, 1, 262144, 4, 128, 1) - 2304
     assert w2 == 2 * w1 == 2 * 2 * 131072 * 4 * 4
 
 

@@ -253,9 +253,13 @@ def test_persistent_launch_equals_one_tile_per_workgroup(shape, lengths, causal)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(lse1, lse2), "forward, dirty workspace"
     assert torch.equal(o1, o3) and torch.equal(lse1, lse3), "forward, workspace reused"
-    # the queue counters (nine ints at the workspace's start) are left cleared; the rest is untouched
-    assert torch.count_nonzero(fws[:36]).item() == 0, "the forward leaves its counters cleared"
-    assert torch.all(fws[36:] == 0xFF).item(), "the forward writes only its counters"
+    # the queue counters (nine ints, 128 bytes apart) are left cleared; the rest is untouched
+    words = fws.view(torch.int32)
+    ctr = torch.zeros_like(words, dtype=torch.bool)
+    ctr[0::32] = True
+    assert int(ctr.sum()) == 9
+    assert torch.count_nonzero(words[ctr]).item() == 0, "the forward leaves its counters cleared"
+    assert torch.all(words[~ctr] == -1).item(), "the forward writes only its counters"
     ws = torch.full((uly.ulysses_attn_bwd_workspace_bytes(*shape, torch.bfloat16),), 0xFF, dtype=torch.uint8,
                     device=dev)
     g1 = uly.ulysses_attn_bwd(q, k, v, o1, do, lse1, packing, causal, workspace=ws)

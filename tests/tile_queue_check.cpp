@@ -3,7 +3,9 @@
 // every (unit, level, document) tile exactly once, list x only units
 // u = x (mod 8); within a list the level groups come in order (every tile of
 // group g before any of group g + 1) and, within a group, a unit's tiles are
-// contiguous and in level order. Built for the host only and run by
+// contiguous and in level order; and the first tiles handed out by workgroup
+// index and the counter's claims together cover each list once. Built for the
+// host only and run by
 // tests/test_tile_queue_cpu.py.
 #include <cstdio>
 #include <set>
@@ -47,6 +49,25 @@ int main() {
         }
         if ((int)seen.size() != units * nslots * ndoc) ++bad;
       }
+  // First tiles by workgroup index: for every grid size, the workgroups
+  // b = x (mod 8) take tiles b / 8 of list x, exactly the first
+  // queue_static_count(x, grid, n) of them, and the counter's claims
+  // (static count + 0, 1, ...) hand out the rest, each once.
+  for (int grid = 1; grid <= 300; ++grid)
+    for (int n : {0, 1, 5, 31, 32, 33, 64, 100, 1000}) {
+      ++cases;
+      for (int x = 0; x < kUnitGroup; ++x) {
+        std::set<int> got;
+        for (int b = x; b < grid; b += kUnitGroup)
+          if (b / kUnitGroup < n && !got.insert(b / kUnitGroup).second) ++bad;
+        const int nst = queue_static_count(x, grid, n);
+        if ((int)got.size() != nst) ++bad;
+        for (int c = 0; nst + c < n; ++c)
+          if (!got.insert(nst + c).second) ++bad;
+        if ((int)got.size() != n) ++bad;
+        if (!got.empty() && (*got.begin() != 0 || *got.rbegin() != n - 1)) ++bad;
+      }
+    }
   std::printf("tile queue geometries %d, mismatches %d\n", cases, bad);
   return bad != 0;
 }

@@ -307,7 +307,7 @@ def ulysses_attn_bwd_prepared(q, k, v, dout, lse, workspace, cu_seqlens=None, ca
 
 
 # The fixed per-GPU scratch of ulysses_attn_bwd_noalloc (ULY_NOALLOC_SCRATCH_BYTES in ulysses.h).
-ULY_NOALLOC_SCRATCH_BYTES = (64 << 20) + 256
+ULY_NOALLOC_SCRATCH_BYTES = (64 << 20) + 2304
 
 
 def ulysses_attn_bwd_noalloc(q, k, v, o, dout, lse, cu_seqlens=None, causal: bool = True, dq=None, dk=None,

@@ -123,9 +123,8 @@ __device__ __forceinline__ void doc_range(const BwdArgs& a, int doc, int& s, int
 // O and dO stream through once) issued before the first product.
 constexpr int kDeltaPasses = 4;
 // Tile-queue counters of a persistent backward, at the end of the workspace:
-// the dK/dV kernel's at [0, kQueueInts), the dQ kernel's at [16, 16 + kQueueInts).
-constexpr int kSchedInts = 32;
-constexpr int kSchedDq = 16;
+// the dK/dV kernel's queue (kQueueBytes), then the dQ kernel's.
+constexpr int kSchedDq = kQueueBytes / 4;
 typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_nt16(const bf16* p) {
   return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
@@ -139,7 +138,8 @@ __global__ __launch_bounds__(kThreads) void delta_bf16_kernel(const bf16* __rest
                                                               float* __restrict__ lse2, int N, int Hl,
                                                               long long units, int* __restrict__ sched) {
   // the tile-queue counters of the dK/dV and dQ kernels start at zero
-  if (sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kSchedInts) sched[threadIdx.x] = 0;
+  if (sched && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < 2 * kQueueInts)
+    sched[(threadIdx.x < kQueueInts ? 0 : kSchedDq) + (threadIdx.x % kQueueInts) * kCtrStride] = 0;
   constexpr int LPR = D / 8;              // lanes per row
   constexpr int RPP = kThreads / LPR;     // rows per pass
   const int sub = threadIdx.x % LPR;
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
   __shared__ __attribute__((aligned(16))) bf16 k1s[TILE];
   __shared__ __attribute__((aligned(16))) bf16 v1s[TILE];
 
-  __shared__ int s_claim[2];
+  __shared__ int s_claim[4];
   TileQueue tq;
   tq.init(a.sched, a.nslots, a.ndoc, a.units);
   TileId tid_;
@@ -361,6 +361,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
       step(t, k0s, v0s, k1s, v1s);
       if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
     }
+    tq.prefetch();  // the next tile's claim goes out before this one's stores
 
     if (qvalid) {
       bf16* out = a.dq + base + (size_t)qi * rs;
@@ -381,6 +382,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
             *reinterpret_cast<uint2*>(out + cb * 32 + 8 * gq + 4 * half) = pack4_scaled(dqacc[cb], 4 * gq, a.scale);
       }
     }
+    tq.publish(s_claim);  // (its wait for the claim does not wait for the stores)
   }
   tq.finish();
 }
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kKvThreads, 1) void attn_dkdv_bf16_kernel(BwdArgs a
   // P and dS of the last tile: per producer, per query block, 4 MFMA operands of 64 lanes
   __shared__ __attribute__((aligned(16))) uint4 xbuf[4 * 2 * 4 * 64];
 
-  __shared__ int s_claim[2];
+  __shared__ int s_claim[4];
   TileQueue tq;
   tq.init(a.sched, a.nslots, a.ndoc, a.units);
   // The wave index is the same in every lane; saying so keeps the role
@@ -799,7 +801,7 @@ int device_cu_count() {
 
 // The queue counters behind the 2 * rows floats of a backward workspace
 // (256-byte aligned offset; ulysses_attn_bwd_workspace_bytes counts them).
-constexpr size_t kSchedBytes = 256;
+constexpr size_t kSchedBytes = 2 * uly::kQueueBytes;
 inline size_t sched_offset(size_t rows) { return (2 * rows * sizeof(float) + 255) / 256 * 256; }
 int* sched_counters(float* ws, size_t rows) {
   return reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + sched_offset(rows));

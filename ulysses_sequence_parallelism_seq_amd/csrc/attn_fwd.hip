@@ -108,7 +108,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) bf16 v1s[S::TILE];
 
   // ---- which tile
-  __shared__ int s_claim[2];
+  __shared__ int s_claim[4];
   TileQueue tq;
   tq.init(a.sched, a.nq_slots, a.ndoc, a.units);
   TileId tid_;
@@ -300,11 +300,20 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         // O^T += V^T P^T: the A operand is V^T read from the row-major V tile
         // with transposing reads; step (blk, mm) covers keys blk*32 + 16*mm ..
         // +15 in the accumulator's row order, which is how P^T sits in pb.
+        // V^T fragment m (column block m / (2 NB), step m % (2 NB)) is read PF
+        // MFMAs ahead of its use, the distance held by scheduling barriers (left
+        // to itself, the scheduler has placed each fragment's reads right before
+        // its MFMA, one LDS latency per MFMA)
+        constexpr int NV = CB * 2 * NB;
+        bf16x8 vf[PF + 1];
   #pragma unroll
-        for (int cb = 0; cb < CB; ++cb)
+        for (int m = 0; m < PF; ++m) vf[m] = a_from_rows_at<D>(vs, fo, m % (2 * NB), m / (2 * NB));
   #pragma unroll
-          for (int st = 0; st < 2 * NB; ++st)
-            oacc[cb] = mfma32(a_from_rows_at<D>(vs, fo, st, cb), as_bf16x8(pb[st]), oacc[cb]);
+        for (int m = 0; m < NV; ++m) {
+          if (m + PF < NV) vf[(m + PF) % (PF + 1)] = a_from_rows_at<D>(vs, fo, (m + PF) % (2 * NB), (m + PF) / (2 * NB));
+          oacc[m / (2 * NB)] = mfma32(vf[m % (PF + 1)], as_bf16x8(pb[m % (2 * NB)]), oacc[m / (2 * NB)]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
 
       wait_vmem();
@@ -314,6 +323,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       step(t, k0s, v0s, k1s, v1s);
       if (t + 1 < ntiles) step(t + 1, k1s, v1s, k0s, v0s);
     }
+    tq.prefetch();  // the next tile's claim goes out before this one's stores
 
     // ---- normalise and write O (one query per lane, 4 consecutive columns per store) and lse
     const float l_tot = l_run + swap_halves(l_run);
@@ -341,6 +351,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       if (half == 0) a.lse[(size_t)unit * a.N + qi] = (m_run + log2f(l_tot)) * kLn2;
     }
+    tq.publish(s_claim);  // (its wait for the claim does not wait for the stores)
   }
   tq.finish();
 }
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 // Clears a persistent launch's queue counters (a kernel rather than a memset,
 // so that the call can be captured in a graph).
 __global__ void sched_clear_kernel(int* p) {
-  if (threadIdx.x < kQueueInts) p[threadIdx.x] = 0;
+  if (threadIdx.x < kQueueInts) p[threadIdx.x * kCtrStride] = 0;
 }
 
 }  // namespace
@@ -465,7 +476,7 @@ extern "C" int ulysses_attn_fwd(const void* q, const void* k, const void* v, voi
                   stream);
 }
 
-extern "C" size_t ulysses_attn_fwd_workspace_bytes(void) { return 256; }
+extern "C" size_t ulysses_attn_fwd_workspace_bytes(void) { return kQueueBytes; }
 
 extern "C" int ulysses_attn_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                                    void* workspace, size_t workspace_bytes, const int* cu_seqlens, int ndoc,

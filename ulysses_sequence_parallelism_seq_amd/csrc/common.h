@@ -287,12 +287,21 @@ __device__ __forceinline__ TileId decode_tile(int bid, int nslots, int ndoc, int
 // tiles come before any unit's shortest ones, so the list ends with short
 // tiles even when an XCD has few tiles per workgroup. A workgroup takes from
 // its own XCD's list while it lasts, then from the others' lists: XCDs that
-// run at a higher clock take over the work of slower ones instead of idling. Claims are atomic adds on counters in caller memory;
-// each tile is still computed whole by one workgroup, so the results do not
-// depend on the assignment. The last workgroup to finish sets the counters
-// back to zero for the next launch on the same memory.
+// run at a higher clock take over the work of slower ones instead of idling.
+// A workgroup's first tile is the one its index names (workgroup b: tile
+// b / 8 of list b mod 8, the list of the XCD the hardware deals it to); later
+// tiles are claimed with atomic adds on counters in caller memory, one
+// 128-byte line per counter (the 256 claims at the end of the first tiles
+// would otherwise queue on one line); the forward and dQ kernels send the
+// next claim before the current tile's results are written (prefetch,
+// publish). Each tile is still computed whole by
+// one workgroup, so the results do not depend on the assignment. The last
+// workgroup to finish sets the counters back to zero for the next launch on
+// the same memory.
 // With ctr == nullptr a workgroup handles the one tile blockIdx.x names.
-constexpr int kQueueInts = 9;  // 8 claim counters, then the count of finished workgroups
+constexpr int kQueueInts = 9;   // 8 claim counters, then the count of finished workgroups
+constexpr int kCtrStride = 32;  // ints from one counter to the next
+constexpr int kQueueBytes = kQueueInts * kCtrStride * 4;
 constexpr int kLevelGroups = 4;
 
 // Tiles in the list of XCD x (the units u = x mod 8 of `units`).
@@ -322,12 +331,24 @@ __host__ __device__ __forceinline__ TileId queue_decode(int x, int i, int units,
   return t;
 }
 
+typedef __attribute__((address_space(1))) int global_int;
+// Tiles of a list of n handed out by workgroup index in a grid of `grid`
+// workgroups: workgroup b takes tile b / 8 of list b mod 8, so list x gets one
+// per workgroup b = x (mod 8) while it lasts; its counter hands out the rest.
+__host__ __device__ __forceinline__ int queue_static_count(int x, int grid, int n) {
+  return min((grid - x + 7) >> 3, n);
+}
+
 struct TileQueue {
   int* ctr;
   int nslots, ndoc, units;
   int x0;         // this workgroup's XCD
   unsigned live;  // lists not yet found exhausted (thread 0)
-  bool pending;   // one-tile mode: the tile is still to be handed out
+  int pre;        // thread 0: counter value claimed ahead from list x0
+  bool has_pre;   // thread 0: pre holds a claim not yet used
+  bool ready;     // thread 0: the coming next() call's tile is already in s_claim
+  int calls;      // next() calls so far: the first hands out the tile named by
+                  // blockIdx.x (both modes); the parity picks the s_claim pair
 
   __device__ __forceinline__ void init(int* c, int nslots_, int ndoc_, int units_) {
     ctr = c;
@@ -336,38 +357,93 @@ struct TileQueue {
     units = units_;
     x0 = __builtin_amdgcn_s_getreg((15 << 11) | 20) & 7;  // HW_REG_XCC_ID
     live = 0xffu;
-    pending = true;
+    pre = 0;
+    has_pre = false;
+    ready = false;
+    calls = 0;
   }
   __device__ __forceinline__ int list_len(int x) const { return queue_list_len(x, units, nslots, ndoc); }
-  // The next tile of this workgroup; false when there is none. Workgroup-
-  // uniform; contains barriers in the persistent mode (every thread calls it).
-  __device__ __forceinline__ bool next(TileId& t, int* s_claim) {
-    if (!ctr) {
-      if (!pending) return false;
-      pending = false;
-      t = decode_tile(blockIdx.x, nslots, ndoc, units);
-      return true;
-    }
-    __syncthreads();  // every wave is done with the previous tile and with s_claim
-    if (threadIdx.x == 0) {
-      int cx = -1, ct = 0;
-      for (int k = 0; k < kUnitGroup && cx < 0; ++k) {
-        const int x = (x0 + k) & 7;
-        if (!((live >> x) & 1u)) continue;
-        const int n = list_len(x);
-        const int i = n > 0 ? atomicAdd(&ctr[x], 1) : 0;
-        if (i < n) {
-          cx = x;
-          ct = i;
-        } else {
-          live &= ~(1u << x);
-        }
+  __device__ __forceinline__ int static_count(int x) const {
+    return queue_static_count(x, (int)gridDim.x, list_len(x));
+  }
+  // Thread 0: one atomic claim on list x's counter; the tile index is the
+  // value plus static_count(x) (the list's length when the workgroup indices
+  // already cover the list: no atomic then).
+  __device__ __forceinline__ int claim_raw(int x) const {
+    if (static_count(x) >= list_len(x)) return list_len(x);
+    // The address goes through a vector register: with a uniform one the
+    // compiler combines the lanes' adds and broadcasts the result at once,
+    // which waits for the atomic right where it is issued.
+    global_int* p = (global_int*)(ctr + x * kCtrStride);
+    asm volatile("" : "+v"(p));
+    return __hip_atomic_fetch_add(p, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  // Thread 0: the next tile (own list first, then the others') into the
+  // s_claim pair of next() call c.
+  __device__ __forceinline__ void resolve(int* s_claim, int c) {
+    int cx = -1, ct = 0;
+    for (int k = 0; k < kUnitGroup && cx < 0; ++k) {
+      const int x = (x0 + k) & 7;
+      if (!((live >> x) & 1u)) continue;
+      const int i = ((k == 0 && has_pre) ? pre : claim_raw(x)) + static_count(x);
+      if (k == 0) has_pre = false;
+      if (i < list_len(x)) {
+        cx = x;
+        ct = i;
+      } else {
+        live &= ~(1u << x);
       }
-      s_claim[0] = cx;
-      s_claim[1] = ct;
     }
-    __syncthreads();
-    const int x = s_claim[0], i = s_claim[1];
+    s_claim[2 * (c & 1)] = cx;
+    s_claim[2 * (c & 1) + 1] = ct;
+  }
+  // The claim of the next tile, in two steps that let its latency pass
+  // behind the current tile's work: prefetch() sends the atomic add on the
+  // workgroup's own list (early in the tile's last step), publish() puts the
+  // next tile into shared memory (once the tile's math is done, before its
+  // results are stored, so that the wait for the add's return does not also
+  // wait for those stores). Both are for every thread to call; only thread 0
+  // acts, and only in the persistent mode.
+  __device__ __forceinline__ void prefetch() {
+    if (ctr && threadIdx.x == 0 && !has_pre && !ready && ((live >> x0) & 1u)) {
+      pre = claim_raw(x0);
+      has_pre = true;
+    }
+  }
+  __device__ __forceinline__ void publish(int* s_claim) {
+    if (ctr && threadIdx.x == 0 && !ready) {
+      resolve(s_claim, calls);
+      ready = true;
+    }
+  }
+  // The next tile of this workgroup; false when there is none. Workgroup-
+  // uniform; in the persistent mode every thread calls it and every call after
+  // the first has one barrier. s_claim: four ints of shared memory, used in
+  // two pairs by turns, so that a pair is rewritten only after every wave has
+  // passed the barrier that follows its reading.
+  __device__ __forceinline__ bool next(TileId& t, int* s_claim) {
+    const int c = calls++;
+    if (c == 0) {
+      const int x = blockIdx.x & 7, i = blockIdx.x >> 3;
+      if (!ctr) {
+        t = decode_tile(blockIdx.x, nslots, ndoc, units);
+        return true;
+      }
+      if (i < list_len(x)) {
+        t = queue_decode(x, i, units, nslots, ndoc);
+        return true;
+      }
+    }
+    if (!ctr) return false;
+    if (threadIdx.x == 0) {
+      if (!ready) resolve(s_claim, c);
+      ready = false;
+    }
+    barrier_lds_only();
+    // the same in every lane: saying so keeps the tile's coordinates, and all
+    // the addresses and buffer descriptors derived from them, scalar
+    const int x = __builtin_amdgcn_readfirstlane(s_claim[2 * (c & 1)]);
+    const int i = __builtin_amdgcn_readfirstlane(s_claim[2 * (c & 1) + 1]);
     if (x < 0) return false;
     t = queue_decode(x, i, units, nslots, ndoc);
     return true;
@@ -375,8 +451,10 @@ struct TileQueue {
   // After the last next(): counts this workgroup out; the last one resets the counters.
   __device__ __forceinline__ void finish() {
     if (!ctr || threadIdx.x != 0) return;
-    if (__hip_atomic_fetch_add(&ctr[8], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == (int)gridDim.x - 1) {
-      for (int x = 0; x < kQueueInts; ++x) __hip_atomic_store(&ctr[x], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__hip_atomic_fetch_add(&ctr[8 * kCtrStride], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) ==
+        (int)gridDim.x - 1) {
+      for (int x = 0; x < kQueueInts; ++x)
+        __hip_atomic_store(&ctr[x * kCtrStride], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 };
