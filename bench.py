@@ -3,11 +3,11 @@
 One step = one Ulysses attention layer, forward and backward, for all sp
 virtual ranks of the workload held on this GPU (default: the long-context
 workload, B=1, N=131072, H=32, sp=8, d=128, bf16, causal):
-  seq_to_head(q), (k), (v)          8 shards [16384, 32, 128] -> 8 shares [131072, 4, 128]
+  seq_to_head(q, k, v)  (one launch) 8 shards [16384, 32, 128] -> 8 shares [131072, 4, 128]
   attn_fwd over the 8 shares         saves lse only
   head_to_seq(o), seq_to_head(dO)
   attn_bwd over the 8 shares         D pre-pass, then dK/dV + dQ kernels (two calls)
-  head_to_seq(dq), (dk), (dv)
+  head_to_seq(dq, dk, dv)  (one launch)
 Inputs are seeded synthetic tensors already resident in HBM. The timed steps
 (wall clock between two device synchronisations) carry HIP events around the
 backward call alone, the roofline's kernel; a second pass of as many steps
@@ -162,9 +162,8 @@ def step(w, bufs, packing, timer=None):
     o, lse, dq, dk, dv = bufs["head_out"]
     os_, dqs, dks, dvs = bufs["seq_out"]
     ws = bufs["ws"]
-    run("seq_to_head", lambda: uly.ulysses_seq_to_head(qs, out=qh))
-    run("seq_to_head", lambda: uly.ulysses_seq_to_head(ks, out=kh))
-    run("seq_to_head", lambda: uly.ulysses_seq_to_head(vs, out=vh))
+    # q, k and v go into the exchange together: one launch for the three
+    run("seq_to_head_x3", lambda: uly.ulysses_seq_to_head_n([qs, ks, vs], [qh, kh, vh]))
     run("attn_fwd", lambda: uly.ulysses_attn_fwd(qh, kh, vh, packing, w.causal, out=o, lse=lse,
                                                  workspace=bufs["fws"]))
     run("head_to_seq", lambda: uly.ulysses_head_to_seq(o, out=os_))
@@ -175,9 +174,7 @@ def step(w, bufs, packing, timer=None):
         run("attn_bwd_prepared", lambda: uly.ulysses_attn_bwd_prepared(qh, kh, vh, doh, lse, ws, packing,
                                                                        w.causal, dq=dq, dk=dk, dv=dv))
     run("attn_bwd", bwd)
-    run("head_to_seq", lambda: uly.ulysses_head_to_seq(dq, out=dqs))
-    run("head_to_seq", lambda: uly.ulysses_head_to_seq(dk, out=dks))
-    run("head_to_seq", lambda: uly.ulysses_head_to_seq(dv, out=dvs))
+    run("head_to_seq_x3", lambda: uly.ulysses_head_to_seq_n([dq, dk, dv], [dqs, dks, dvs]))
 
 
 def make_ring_buffers(w: workloads.Workload, dev):
@@ -389,6 +386,10 @@ def main():
                 k: round(v / (avg["seq_to_head" if k.endswith("head") else "head_to_seq"] * 1e-3) / 1e9, 1)
                 for k, v in traffic["permute"].items()},
             "permute_algorithmic_bytes": 2 * tensor_bytes,
+            # q, k, v (dq, dk, dv) in one launch of ulysses_seq_to_head_n (head_to_seq_n)
+            "permute_x3_ms": {k: round(avg[k], 4) for k in ("seq_to_head_x3", "head_to_seq_x3")},
+            "permute_x3_gbs": {k: round(3 * 2 * tensor_bytes / (avg[k] * 1e-3) / 1e9, 1)
+                               for k in ("seq_to_head_x3", "head_to_seq_x3")},
             "value_12d_no_recompute": round(12 * w.d * pairs / (ms_per_step * 1e-3) / 1e12, 2),
             "flops_per_step": flops_step,
             "calls_timed": counts,

@@ -89,6 +89,22 @@ int ulysses_head_to_seq(const void* x_head, void* x_seq, int B, int N, int H, in
                         int dtype, void* stream);
 
 /*
+ * The same two layout changes for n tensors of one shape in one launch (q, k
+ * and v going into an exchange, dq, dk and dv coming out of it; the guide's
+ * layout diagram applies to each): x_seq[i] -> x_head[i] (resp. x_head[i] ->
+ * x_seq[i]) for i < n, each exactly as one ulysses_seq_to_head
+ * (ulysses_head_to_seq) call. x_seq and x_head are host arrays of n device
+ * pointers, read during the call only; 1 <= n <= 4.
+ * Errors: ULY_EINVAL also when n is out of range, an array or one of its
+ * pointers is null, or an output overlaps any input or another output;
+ * ULY_ESHAPE also when n * sp > 65535; otherwise as ulysses_seq_to_head.
+ */
+int ulysses_seq_to_head_n(const void* const* x_seq, void* const* x_head, int n, int B, int N, int H,
+                          int d, int sp, int dtype, void* stream);
+int ulysses_head_to_seq_n(const void* const* x_head, void* const* x_seq, int n, int B, int N, int H,
+                          int d, int sp, int dtype, void* stream);
+
+/*
  * Attention forward over the head-sharded shares of sp virtual ranks
  * (congresoia365 article, "Cómo Funciona Ulysses", local attention step).
  * For every (rank, batch row, head), with scale = 1/sqrt(d):

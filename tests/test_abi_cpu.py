@@ -28,7 +28,8 @@ def test_library_exports_every_declared_function():
     lib = uly.library()
     names = declared_functions()
     assert set(names) == {
-        "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_bwd",
+        "ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_n", "ulysses_head_to_seq_n",
+        "ulysses_attn_fwd", "ulysses_attn_bwd",
         "ulysses_attn_fwd_ws", "ulysses_attn_fwd_workspace_bytes",
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_attn_bwd_noalloc",
         "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
@@ -62,6 +63,30 @@ def test_permute_argument_errors():
     # 16-byte accesses: misaligned buffers are rejected
     assert f(ctypes.c_void_p(0x1002), ctypes.c_void_p(0x100000), 1, 8, 4, 64, 2, 1, None) == EINVAL
     assert g(FAKE, ctypes.c_void_p(0x100008), 1, 8, 4, 64, 2, 1, None) == EINVAL
+
+
+def test_batched_permute_argument_errors():
+    """ulysses_seq_to_head_n / ulysses_head_to_seq_n reject what the header lists before any launch."""
+    lib = uly.library()
+
+    def arr(*ps):
+        return (ctypes.c_void_p * len(ps))(*ps)
+
+    a, b, c, d_ = 0x100000, 0x200000, 0x300000, 0x400000  # 4 KiB tensors (1, 8, 4, 64, bf16)
+    for f in (lib.ulysses_seq_to_head_n, lib.ulysses_head_to_seq_n):
+        assert f(arr(a, b), arr(c, d_), 0, 1, 8, 4, 64, 2, 1, None) == EINVAL  # n < 1
+        assert f(arr(a, b, a, b, a), arr(c, d_, c, d_, c), 5, 1, 8, 4, 64, 2, 1, None) == EINVAL  # n > 4
+        assert f(None, arr(c, d_), 2, 1, 8, 4, 64, 2, 1, None) == EINVAL
+        assert f(arr(a, b), None, 2, 1, 8, 4, 64, 2, 1, None) == EINVAL
+        assert f(arr(a, None), arr(c, d_), 2, 1, 8, 4, 64, 2, 1, None) == EINVAL
+        assert f(arr(a, b), arr(c, c + 64), 2, 1, 8, 4, 64, 2, 1, None) == EINVAL  # outputs overlap
+        assert f(arr(a, b), arr(c, a + 64), 2, 1, 8, 4, 64, 2, 1, None) == EINVAL  # output on an input
+        assert f(arr(a, b), arr(c + 8, d_), 2, 1, 8, 4, 64, 2, 1, None) == EINVAL  # misaligned
+        assert f(arr(a, b), arr(c, d_), 2, 1, 9, 4, 64, 2, 1, None) == ESHAPE  # N % sp
+        assert f(arr(a, b), arr(c, d_), 2, 1, 8, 4, 96, 2, 1, None) == EUNSUP  # d
+        # n * sp beyond the grid's z (tensors 1 TiB apart, one token per shard)
+        t = 1 << 40
+        assert f(arr(t, 2 * t), arr(3 * t, 4 * t), 2, 1, 32768, 32768, 64, 32768, 1, None) == ESHAPE
 
 
 def test_attention_argument_errors():

@@ -48,6 +48,29 @@ def test_permute_bit_exact(sp, B, Ns, H, d, dtype):
     assert np.array_equal(seq.cpu().view(ibits).numpy(), oracle.head_to_seq(y.view(ibits).numpy()))
 
 
+@pytest.mark.parametrize("n,sp,B,Ns,H,d,dtype", [
+    (3, 4, 2, 1024, 32, 128, "bf16"),  # q, k, v of the llama7b workload (full size)
+    (4, 3, 1, 9, 9, 64, "fp32"),       # neither sp nor the run a power of two
+    (2, 2, 1, 10, 6, 64, "bf16"),
+    (1, 8, 1, 33, 16, 128, "bf16"),
+])
+def test_batched_permute_bit_exact(n, sp, B, Ns, H, d, dtype):
+    """n tensors in one launch: each output equals the oracle's layout change of its input."""
+    say("batched permute", n, sp, B, Ns, H, d, dtype)
+    dev = device()
+    ibits = torch.int16 if dtype == "bf16" else torch.int32
+    xs = [workloads.random_bits((sp, B, Ns, H, d), seed=40 + i, dtype=dtype) for i in range(n)]
+    heads = uly.ulysses_seq_to_head_n([x.to(dev) for x in xs])
+    torch.cuda.synchronize()
+    for x, h in zip(xs, heads):
+        assert np.array_equal(h.cpu().view(ibits).numpy(), oracle.seq_to_head(x.view(ibits).numpy()))
+    ys = [workloads.random_bits((sp, B, Ns * sp, H // sp, d), seed=50 + i, dtype=dtype) for i in range(n)]
+    seqs = uly.ulysses_head_to_seq_n([y.to(dev) for y in ys])
+    torch.cuda.synchronize()
+    for y, q in zip(ys, seqs):
+        assert np.array_equal(q.cpu().view(ibits).numpy(), oracle.head_to_seq(y.view(ibits).numpy()))
+
+
 # ------------------------------------------------------------ fp32 exactness
 
 

@@ -10,6 +10,8 @@ missing library is an error.
 Functions carry the C names:
   ulysses_seq_to_head(x_seq, sp)          [sp,B,N/sp,H,d] -> [sp,B,N,H/sp,d]
   ulysses_head_to_seq(x_head, sp)         [sp,B,N,H/sp,d] -> [sp,B,N/sp,H,d]
+  ulysses_seq_to_head_n(xs), ulysses_head_to_seq_n(xs)  the same for up to four
+                                          tensors of one shape in one launch
   ulysses_attn_fwd(q, k, v, ...)          -> (o, lse)  (bf16: the persistent launch of
                                           ulysses_attn_fwd_ws unless persistent=False)
   ulysses_attn_fwd_workspace_bytes()
@@ -66,6 +68,8 @@ def library() -> ctypes.CDLL:
         vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
         lib.ulysses_seq_to_head.argtypes = [vp, vp, i, i, i, i, i, i, vp]
         lib.ulysses_head_to_seq.argtypes = [vp, vp, i, i, i, i, i, i, vp]
+        lib.ulysses_seq_to_head_n.argtypes = [vp, vp] + [i] * 7 + [vp]
+        lib.ulysses_head_to_seq_n.argtypes = [vp, vp] + [i] * 7 + [vp]
         lib.ulysses_attn_fwd.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, vp]
         lib.ulysses_attn_fwd_workspace_bytes.argtypes = []
         lib.ulysses_attn_fwd_workspace_bytes.restype = sz
@@ -90,7 +94,8 @@ def library() -> ctypes.CDLL:
         lib.ulysses_tiled_mlp_bwd.argtypes = [vp] * 10 + [sz] + [i] * 4 + [vp]
         lib.ulysses_status_string.argtypes = [i]
         lib.ulysses_status_string.restype = ctypes.c_char_p
-        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_attn_fwd", "ulysses_attn_fwd_ws",
+        for name in ("ulysses_seq_to_head", "ulysses_head_to_seq", "ulysses_seq_to_head_n",
+                     "ulysses_head_to_seq_n", "ulysses_attn_fwd", "ulysses_attn_fwd_ws",
                      "ulysses_attn_bwd",
                      "ulysses_attn_bwd_noalloc", "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
                      "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
@@ -164,6 +169,58 @@ def ulysses_head_to_seq(x_head: torch.Tensor, out: torch.Tensor | None = None) -
     _check("ulysses_head_to_seq", library().ulysses_head_to_seq(
         _ptr(x_head), _ptr(out), B, N, Hl * sp, d, sp, _dtype_code(x_head), _stream(x_head)))
     return out
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def ulysses_seq_to_head_n(xs_seq, outs=None):
+    """ulysses_seq_to_head of up to four tensors of one shape in one launch (bit-exact)."""
+    xs_seq = list(xs_seq)
+    if not 1 <= len(xs_seq) <= 4:
+        raise ValueError("one to four tensors")
+    sp, B, Ns, H, d = xs_seq[0].shape
+    if H % sp:
+        raise ValueError("H must be divisible by sp")
+    shape = (sp, B, Ns * sp, H // sp, d)
+    if outs is None:
+        outs = [torch.empty(shape, dtype=x.dtype, device=x.device) for x in xs_seq]
+    outs = list(outs)
+    if len(outs) != len(xs_seq):
+        raise ValueError("as many outputs as inputs")
+    for x, o in zip(xs_seq, outs):
+        _expect(x, xs_seq[0].shape, xs_seq[0].dtype, "inputs")
+        _expect(o, shape, xs_seq[0].dtype, "outs")
+        _require_device(x, o)
+    _check("ulysses_seq_to_head_n", library().ulysses_seq_to_head_n(
+        _ptr_array(xs_seq), _ptr_array(outs), len(xs_seq), B, Ns * sp, H, d, sp, _dtype_code(xs_seq[0]),
+        _stream(xs_seq[0])))
+    return outs
+
+
+def ulysses_head_to_seq_n(xs_head, outs=None):
+    """ulysses_head_to_seq of up to four tensors of one shape in one launch (bit-exact)."""
+    xs_head = list(xs_head)
+    if not 1 <= len(xs_head) <= 4:
+        raise ValueError("one to four tensors")
+    sp, B, N, Hl, d = xs_head[0].shape
+    if N % sp:
+        raise ValueError("N must be divisible by sp")
+    shape = (sp, B, N // sp, Hl * sp, d)
+    if outs is None:
+        outs = [torch.empty(shape, dtype=x.dtype, device=x.device) for x in xs_head]
+    outs = list(outs)
+    if len(outs) != len(xs_head):
+        raise ValueError("as many outputs as inputs")
+    for x, o in zip(xs_head, outs):
+        _expect(x, xs_head[0].shape, xs_head[0].dtype, "inputs")
+        _expect(o, shape, xs_head[0].dtype, "outs")
+        _require_device(x, o)
+    _check("ulysses_head_to_seq_n", library().ulysses_head_to_seq_n(
+        _ptr_array(xs_head), _ptr_array(outs), len(xs_head), B, N, Hl * sp, d, sp, _dtype_code(xs_head[0]),
+        _stream(xs_head[0])))
+    return outs
 
 
 class DocPacking:
@@ -537,6 +594,8 @@ __all__ = [
     "library",
     "ulysses_seq_to_head",
     "ulysses_head_to_seq",
+    "ulysses_seq_to_head_n",
+    "ulysses_head_to_seq_n",
     "ulysses_attn_fwd",
     "ulysses_attn_fwd_workspace_bytes",
     "ulysses_attn_bwd",
