@@ -33,11 +33,15 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
-# Per-source extra flags. The forward kernel runs about 2% faster with the
-# scheduler's max-ilp strategy (measured per kernel with rocprofv3 on the long
-# workload); the backward kernels are about 1% slower with it, so only the
-# forward's source takes it.
-FILE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# Per-source extra flags: the scheduler's max-ilp strategy. The forward
+# kernel runs about 2% faster with it (measured per kernel with rocprofv3 on
+# the long workload); the backward kernels, in their current form, 1.3%
+# faster on the llama7b workload and 0.1% on the long one (same-box A/Bs,
+# bit-identical outputs).
+FILE_FLAGS = {
+    "attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
 
 
 def _run(cmd, verbose):
