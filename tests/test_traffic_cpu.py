@@ -54,11 +54,14 @@ def test_calibrated_bytes_and_staleness(tmp_path, fake_library):
     # the 1 GiB copies read and write 1 GiB; FETCH_SIZE reports half of that, WRITE_SIZE all
     # of it; a small copy of another grid size does not enter the calibration
     fetch = {"__amd_rocclr_copyBuffer": [(131072, 524288.0), (131072, 524288.0), (64, 3.0)],
-             "permute_seq_to_head": [524300.0, 524300.0], "permute_head_to_seq": [524290.0],
+             # a launch of three tensors (three times the grid) does not enter the per-tensor figure
+             "permute_seq_to_head": [524300.0, 524300.0, (3072, 3 * 524300.0)],
+             "permute_head_to_seq": [524290.0, (3072, 3 * 524290.0)],
              "attn_dkdv_bf16_kernel<128,false>": [900.0, 1100.0],
              "attn_dq_bf16_kernel<128,false>": [500.0], "delta_bf16_kernel<128>": [50.0]}
     write = {"__amd_rocclr_copyBuffer": [(131072, 1048576.0), (64, 9.0)],
-             "permute_seq_to_head": [1048580.0], "permute_head_to_seq": [1048576.0],
+             "permute_seq_to_head": [1048580.0, (3072, 3 * 1048580.0)],
+             "permute_head_to_seq": [1048576.0, (3072, 3 * 1048576.0)],
              "attn_dkdv_bf16_kernel<128,false>": [10.0],
              "attn_dq_bf16_kernel<128,false>": [5.0], "delta_bf16_kernel<128>": [1.0]}
     _counter_dir(tmp_path / "fetch", "FETCH_SIZE", fetch)

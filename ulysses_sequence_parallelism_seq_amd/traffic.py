@@ -55,7 +55,9 @@ def _short(name: str) -> str:
 def _per_dispatch(csv_dir: str, counter: str) -> dict:
     """Average counter value per dispatch of each kernel. For the runtime's copy
     kernel only the dispatches of the largest grid (the calibration copies of
-    one whole tensor) count."""
+    one whole tensor) count; for the permute kernels only those of the smallest
+    grid (one tensor per launch: bench.py also moves q, k, v and dq, dk, dv
+    three to a launch)."""
     values = {}
     for path in glob.glob(os.path.join(csv_dir, "**", "*counter_collection.csv"), recursive=True):
         with open(path) as f:
@@ -68,6 +70,9 @@ def _per_dispatch(csv_dir: str, counter: str) -> dict:
     for k, vs in values.items():
         if k == COPY_KERNEL:
             g = max(gs for gs, _ in vs)
+            vs = [x for x in vs if x[0] == g]
+        elif k in PERMUTE_KERNELS:
+            g = min(gs for gs, _ in vs)
             vs = [x for x in vs if x[0] == g]
         out[k] = sum(v for _, v in vs) / len(vs)
     return out
