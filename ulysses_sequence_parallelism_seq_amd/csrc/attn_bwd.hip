@@ -266,6 +266,9 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
 
     const int kend = causal ? min(e, q0 + kDqBQ) : e;
     const int ntiles = (kend - s + kDqBK - 1) / kDqBK;
+    // the last key this wave's queries see (none when they all lie past the
+    // document end: their rows are never stored)
+    const int wave_klast = q0 + 32 * w >= e ? -1 : causal ? q0 + 32 * w + 31 : e - 1;
 
     f32x16 dqacc[CB];
   #pragma unroll
@@ -292,7 +295,7 @@ __global__ __launch_bounds__(kDqThreads, 1) void attn_dq_bf16_kernel(BwdArgs a) 
         dma.issue(rsrc_at(a.v, kt0 + kDqBK), vn);
       }
 
-      if (!causal || kt0 <= q0 + 32 * w + 31) {
+      if (kt0 <= wave_klast) {
         const bool need_mask = (causal && kt0 + kDqBK - 1 > q0) || kt0 + kDqBK > e;
         // one 32-key block at a time: S^T = K Q^T and dP^T = V dO^T (lane = query,
         // element i is key kt0 + blk*32 + 8*(i/4) + 4*half + (i%4)), dS^T, then

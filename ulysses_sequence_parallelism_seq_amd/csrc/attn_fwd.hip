@@ -164,6 +164,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
 
     const int kend = causal ? min(e, q0 + kBQ) : e;
     const int ntiles = (kend - s + kBK - 1) / kBK;
+    // The last key that this wave's queries see: its last query (causal) or
+    // the document's last key; none when all 32 queries lie past the
+    // document end (a ragged last tile), whose rows are never stored.
+    const int wave_klast = q0 + 32 * w >= e ? -1 : causal ? q0 + 32 * w + 31 : e - 1;
 
     f32x16 oacc[CB];
   #pragma unroll
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_bf16_kernel(FwdArgs a) {
         dma.issue(rsrc_at(vb, kt0 + kBK), vn);
       }
 
-      const bool wave_active = !causal || kt0 <= q0 + 32 * w + 31;
+      const bool wave_active = kt0 <= wave_klast;
       if (wave_active) {
         // S^T for the tile's 32-key blocks
         constexpr int NB = kBK / 32;
