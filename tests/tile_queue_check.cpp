@@ -3,7 +3,8 @@
 // every (unit, level, document) tile exactly once, list x only units
 // u = x (mod 8); within a list the level groups come in order (every tile of
 // group g before any of group g + 1) and, within a group, a unit's tiles are
-// contiguous and in level order; and the first tiles handed out by workgroup
+// contiguous, document by document, each document's levels in order; and the
+// first tiles handed out by workgroup
 // index and the counter's claims together cover each list once. Built for the
 // host only and run by
 // tests/test_tile_queue_cpu.py.
@@ -28,11 +29,12 @@ int main() {
         const int lg = (nslots + kLevelGroups - 1) / kLevelGroups;
         for (int x = 0; x < kUnitGroup; ++x) {
           const int n = queue_list_len(x, units, nslots, ndoc);
-          int prev_grp = -1, prev_unit = -1, prev_lvl = -1;
+          int prev_grp = -1, prev_unit = -1, prev_lvl = -1, prev_doc = -1;
           std::set<std::pair<int, int>> units_done;  // (group, unit) finished
           for (int i = 0; i < n; ++i) {
             const TileId t = queue_decode(x, i, units, nslots, ndoc);
             const int grp = t.lvl / lg;
+            const int g0 = grp * lg, g1 = (grp + 1) * lg < nslots ? (grp + 1) * lg : nslots;
             if (t.unit < 0 || t.unit >= units || t.unit % kUnitGroup != x) ++bad;
             if (t.lvl < 0 || t.lvl >= nslots || t.doc < 0 || t.doc >= ndoc) ++bad;
             if (!seen.insert({t.unit, t.lvl, t.doc}).second) ++bad;
@@ -41,10 +43,19 @@ int main() {
               if (units_done.count({grp, t.unit})) ++bad;  // a unit's part is contiguous
               units_done.insert({grp, prev_unit});
             }
-            if (grp == prev_grp && t.unit == prev_unit && t.lvl < prev_lvl) ++bad;  // level order
+            if (grp == prev_grp && t.unit == prev_unit) {
+              // the next tile of the unit's part: the document's next level, or
+              // the next document's first level of the group
+              const bool next_lvl = t.doc == prev_doc && t.lvl == prev_lvl + 1;
+              const bool next_doc = t.doc == prev_doc + 1 && prev_lvl == g1 - 1 && t.lvl == g0;
+              if (!next_lvl && !next_doc) ++bad;
+            } else if (t.doc != 0 || t.lvl != g0) {
+              ++bad;  // a unit's part starts with its first document's first level
+            }
             prev_grp = grp;
             prev_unit = t.unit;
             prev_lvl = t.lvl;
+            prev_doc = t.doc;
           }
         }
         if ((int)seen.size() != units * nslots * ndoc) ++bad;
