@@ -360,8 +360,9 @@ int ulysses_sp_loss(const float* token_loss, const long long* labels, float* ran
  *                  U * silu'(G) and silu(G)); contents on entry ignored
  * bf16 only. hidden and inter must be multiples of 256 (Llama-7B: 4096 and
  * 11008); tokens and tile are any positive sizes (the last tile may be short).
- * Pointers must be 16-byte aligned.
- * Errors: ULY_EINVAL (null pointer, size <= 0), ULY_ESHAPE (hidden or inter
+ * Pointers (workspace included) must be 16-byte aligned.
+ * Errors: ULY_EINVAL (null pointer, size <= 0, a pointer not 16-byte
+ * aligned), ULY_ESHAPE (hidden or inter
  * not a multiple of 256, or 512 * max(hidden, inter) >= 2^31),
  * ULY_EWORKSPACE, ULY_EHIP.
  */

@@ -250,6 +250,12 @@ def test_tiled_mlp_argument_errors():
     assert bwd(*([FAKE] * 8), None, FAKE, need, 300, 256, 512, 128, None) == EINVAL  # dw_down
     assert bwd(*([FAKE] * 9), FAKE, need - 1, 300, 256, 512, 128, None) == EWS
     assert bwd(*([FAKE] * 9), FAKE, need, -1, 256, 512, 128, None) == EINVAL
+    # every pointer must be 16-byte aligned (the kernels' 16-byte loads and stores)
+    odd = ctypes.c_void_p(FAKE.value + 8)
+    assert fwd(FAKE, FAKE, FAKE, FAKE, odd, FAKE, need, 300, 256, 512, 128, None) == EINVAL  # y
+    assert fwd(FAKE, FAKE, FAKE, FAKE, FAKE, odd, need, 300, 256, 512, 128, None) == EINVAL  # workspace
+    assert bwd(*([FAKE] * 8), odd, FAKE, need, 300, 256, 512, 128, None) == EINVAL  # dw_down
+    assert bwd(FAKE, FAKE, FAKE, FAKE, FAKE, odd, FAKE, FAKE, FAKE, FAKE, need, 300, 256, 512, 128, None) == EINVAL
 
 
 FAR = ctypes.c_void_p(1 << 52)  # a second fake buffer far from FAKE: no overlap at these sizes

@@ -36,6 +36,8 @@
 
 #include <math.h>
 
+#include <initializer_list>
+
 #include "common.h"
 
 namespace {
@@ -76,6 +78,18 @@ struct GemmArgs {
 // hardware exp2 and reciprocal; z -> -inf gives 1 / inf = 0.
 __device__ __forceinline__ float sigmoidf_(float z) {
   return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-z * kLog2e));
+}
+
+// Four bf16 values, rounded to nearest even, as one 8-byte store; and back.
+__device__ __forceinline__ void st_bf16x4(bf16* p, const float* v) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
+}
+__device__ __forceinline__ void ld_bf16x4(const bf16* p, float* v) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(u.x << 16);
+  v[1] = __uint_as_float(u.x & 0xffff0000u);
+  v[2] = __uint_as_float(u.y << 16);
+  v[3] = __uint_as_float(u.y & 0xffff0000u);
 }
 
 // Tile order: blockIdx -> XCD x = blockIdx % 8 (round-robin dispatch); XCD x
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(fa[cur][mb], fb[cur][nb], acc[mb][nb]);
+        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(fb[cur][nb], fa[cur][mb], acc[mb][nb]);
     }
   };
 
@@ -231,42 +245,66 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     if (t + 1 < ntiles) step(t + 1, a1s, b1s, a0s, b0s);
   }
 
-  // ---- epilogue. Element i of acc[mb][nb] in lane l is row
-  // m0 + 128 wm + 32 mb + 8 (i / 4) + 4 half + i % 4 and column n of block nb, lane l % 32.
+  // ---- epilogue. The MFMAs take the B fragment as their first operand, so
+  // acc[mb][nb] holds the block transposed: element i of lane l is row
+  // m0 + 128 wm + 32 mb + l % 32 and column 8 (i / 4) + 4 half + i % 4 of
+  // block nb. Each group of four elements is four consecutive columns of one
+  // row, read and written 8 bytes (bf16) or 16 bytes (fp32) at a time.
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
+    const int m = m0 + 128 * wm + 32 * mb + l32;
+    if (m >= p.M) continue;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int m = m0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * half + (i & 3);
-      if (m >= p.M) continue;
+    for (int gq = 0; gq < 4; ++gq) {
+      const int c4 = 8 * gq + 4 * half;  // first of the four columns within a 32-column block
       if constexpr (kGateUp) {
-        const int col = n0 + 32 * wn + l32;  // intermediate unit
-        const size_t o = (size_t)m * p.ldc + col;
-        const float gv = acc[mb][0][i], uv = acc[mb][1][i];
-        const float s = sigmoidf_(gv);
-        const float silu = gv * s;
-        p.act[o] = (bf16)(silu * uv);
-        if constexpr (kEpi == kEpiGateUpSave) {
+        const size_t o = (size_t)m * p.ldc + n0 + 32 * wn + c4;  // intermediate units
+        float a4[4], g4[4], u4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float gv = acc[mb][0][4 * gq + j], uv = acc[mb][1][4 * gq + j];
+          const float s = sigmoidf_(gv);
+          const float silu = gv * s;
+          a4[j] = silu * uv;
           // the backward's two factors, formed from the fp32 G: silu' has a
           // zero (near G = -1.28) where G's bf16 rounding would become a large
           // relative error of dG; rounding the factor itself costs 2^-8 of it
-          p.g[o] = (bf16)(uv * s * (1.0f + gv * (1.0f - s)));
-          p.u[o] = (bf16)silu;
+          g4[j] = uv * s * (1.0f + gv * (1.0f - s));
+          u4[j] = silu;
+        }
+        st_bf16x4(p.act + o, a4);
+        if constexpr (kEpi == kEpiGateUpSave) {
+          st_bf16x4(p.g + o, g4);
+          st_bf16x4(p.u + o, u4);
         }
       } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-          const int col = n0 + 64 * wn + 32 * nb + l32;
-          const size_t o = (size_t)m * p.ldc + col;
-          const float v = acc[mb][nb][i];
+          const size_t o = (size_t)m * p.ldc + n0 + 64 * wn + 32 * nb + c4;
+          float v4[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = acc[mb][nb][4 * gq + j];
           if constexpr (kEpi == kEpiStoreBf16) {
-            static_cast<bf16*>(p.c)[o] = (bf16)v;
+            st_bf16x4(static_cast<bf16*>(p.c) + o, v4);
           } else if constexpr (kEpi == kEpiDGrad) {
-            p.g[o] = (bf16)(v * (float)p.g[o]);  // dG = dA * U * silu'(G)
-            p.u[o] = (bf16)(v * (float)p.u[o]);  // dU = dA * silu(G)
+            float g4[4], u4[4];
+            ld_bf16x4(p.g + o, g4);
+            ld_bf16x4(p.u + o, u4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              g4[j] *= v4[j];  // dG = dA * U * silu'(G)
+              u4[j] *= v4[j];  // dU = dA * silu(G)
+            }
+            st_bf16x4(p.g + o, g4);
+            st_bf16x4(p.u + o, u4);
           } else {  // kEpiAccF32
-            float* c = static_cast<float*>(p.c) + o;
-            *c = p.accumulate ? *c + v : v;
+            float4* c = reinterpret_cast<float4*>(static_cast<float*>(p.c) + o);
+            float4 r = make_float4(v4[0], v4[1], v4[2], v4[3]);
+            if (p.accumulate) {
+              const float4 old = *c;
+              r = make_float4(old.x + r.x, old.y + r.y, old.z + r.z, old.w + r.w);
+            }
+            *c = r;
           }
         }
       }
@@ -324,6 +362,14 @@ int check_mlp(int tokens, int hidden, int inter, int tile) {
   return ULY_OK;
 }
 
+// 16-byte accesses (direct-to-LDS loads, the epilogues' 8- and 16-byte
+// stores) need 16-byte aligned buffers
+bool aligned16(std::initializer_list<const void*> ptrs) {
+  for (const void* q : ptrs)
+    if ((uintptr_t)q & 15) return false;
+  return true;
+}
+
 size_t mlp_ws_bytes(int tokens, int inter, int tile) {
   const long long t = tile < tokens ? tile : tokens;
   return 3 * (size_t)t * inter * sizeof(bf16);
@@ -340,6 +386,7 @@ extern "C" int ulysses_tiled_mlp_fwd(const void* x, const void* w_gate, const vo
                                      void* y, void* workspace, size_t workspace_bytes, int tokens, int hidden,
                                      int inter, int tile, void* stream) {
   if (!x || !w_gate || !w_up || !w_down || !y) return ULY_EINVAL;
+  if (!aligned16({x, w_gate, w_up, w_down, y, workspace})) return ULY_EINVAL;
   const int rc = check_mlp(tokens, hidden, inter, tile);
   if (rc != ULY_OK) return rc;
   if (!workspace || workspace_bytes < mlp_ws_bytes(tokens, inter, tile)) return ULY_EWORKSPACE;
@@ -371,6 +418,7 @@ extern "C" int ulysses_tiled_mlp_bwd(const void* x, const void* w_gate, const vo
                                      void* workspace, size_t workspace_bytes, int tokens, int hidden, int inter,
                                      int tile, void* stream) {
   if (!x || !w_gate || !w_up || !w_down || !dy || !dx || !dw_gate || !dw_up || !dw_down) return ULY_EINVAL;
+  if (!aligned16({x, w_gate, w_up, w_down, dy, dx, dw_gate, dw_up, dw_down, workspace})) return ULY_EINVAL;
   const int rc = check_mlp(tokens, hidden, inter, tile);
   if (rc != ULY_OK) return rc;
   if (!workspace || workspace_bytes < mlp_ws_bytes(tokens, inter, tile)) return ULY_EWORKSPACE;
