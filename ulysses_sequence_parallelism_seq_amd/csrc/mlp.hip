@@ -115,6 +115,13 @@ __device__ __forceinline__ void tile_of(const GemmArgs& p, int& bm, int& bn) {
 template <bool kAK, bool kBK, int kEpi>
 __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   constexpr bool kGateUp = kEpi == kEpiGateUp || kEpi == kEpiGateUpSave;
+  // accumulator blocks transposed (the B fragment as the MFMA's first
+  // operand): a lane then holds four consecutive output columns per group of
+  // four elements, and the epilogue moves 8 or 16 bytes per access. The
+  // recompute epilogue, which writes three bf16 arrays, keeps the plain
+  // blocks (a lane = one column): there the 32 rows x 16 bytes that each
+  // transposed store touches cost more than its fewer instructions save.
+  constexpr bool kTransAcc = kEpi != kEpiGateUpSave;
   constexpr int TILE = kBM * kBKt;  // bf16 elements of one staged operand tile (both layouts)
   __shared__ __attribute__((aligned(16))) bf16 a0s[TILE];
   __shared__ __attribute__((aligned(16))) bf16 b0s[TILE];
@@ -225,7 +232,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) acc[mb][nb] = mfma32(fb[cur][nb], fa[cur][mb], acc[mb][nb]);
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = kTransAcc ? mfma32(fb[cur][nb], fa[cur][mb], acc[mb][nb])
+                                  : mfma32(fa[cur][mb], fb[cur][nb], acc[mb][nb]);
     }
   };
 
@@ -245,6 +254,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
     if (t + 1 < ntiles) step(t + 1, a1s, b1s, a0s, b0s);
   }
 
+  if constexpr (!kTransAcc) {
+    // ---- recompute epilogue, plain blocks: element i of acc[mb][nb] in lane l
+    // is row m0 + 128 wm + 32 mb + 8 (i / 4) + 4 half + i % 4 and column
+    // (intermediate unit) n0 + 32 wn + l % 32, of Wg's rows (nb = 0) and Wu's (nb = 1).
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + 128 * wm + 32 * mb + 8 * (i >> 2) + 4 * half + (i & 3);
+        if (m >= p.M) continue;
+        const size_t o = (size_t)m * p.ldc + n0 + 32 * wn + l32;
+        const float gv = acc[mb][0][i], uv = acc[mb][1][i];
+        const float s = sigmoidf_(gv);
+        const float silu = gv * s;
+        p.act[o] = (bf16)(silu * uv);
+        // the backward's two factors, formed from the fp32 G: silu' has a
+        // zero (near G = -1.28) where G's bf16 rounding would become a large
+        // relative error of dG; rounding the factor itself costs 2^-8 of it
+        p.g[o] = (bf16)(uv * s * (1.0f + gv * (1.0f - s)));
+        p.u[o] = (bf16)silu;
+      }
+    }
+    return;
+  }
   // ---- epilogue. The MFMAs take the B fragment as their first operand, so
   // acc[mb][nb] holds the block transposed: element i of lane l is row
   // m0 + 128 wm + 32 mb + l % 32 and column 8 (i / 4) + 4 half + i % 4 of
@@ -259,24 +292,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
       const int c4 = 8 * gq + 4 * half;  // first of the four columns within a 32-column block
       if constexpr (kGateUp) {
         const size_t o = (size_t)m * p.ldc + n0 + 32 * wn + c4;  // intermediate units
-        float a4[4], g4[4], u4[4];
+        float a4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float gv = acc[mb][0][4 * gq + j], uv = acc[mb][1][4 * gq + j];
-          const float s = sigmoidf_(gv);
-          const float silu = gv * s;
-          a4[j] = silu * uv;
-          // the backward's two factors, formed from the fp32 G: silu' has a
-          // zero (near G = -1.28) where G's bf16 rounding would become a large
-          // relative error of dG; rounding the factor itself costs 2^-8 of it
-          g4[j] = uv * s * (1.0f + gv * (1.0f - s));
-          u4[j] = silu;
+          a4[j] = gv * sigmoidf_(gv) * uv;
         }
         st_bf16x4(p.act + o, a4);
-        if constexpr (kEpi == kEpiGateUpSave) {
-          st_bf16x4(p.g + o, g4);
-          st_bf16x4(p.u + o, u4);
-        }
       } else {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
