@@ -287,48 +287,76 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_bf16_kernel(GemmArgs p) {
   for (int mb = 0; mb < 4; ++mb) {
     const int m = m0 + 128 * wm + 32 * mb + l32;
     if (m >= p.M) continue;
+    const size_t row = (size_t)m * p.ldc;
+    if constexpr (kGateUp) {
 #pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int c4 = 8 * gq + 4 * half;  // first of the four columns within a 32-column block
-      if constexpr (kGateUp) {
-        const size_t o = (size_t)m * p.ldc + n0 + 32 * wn + c4;  // intermediate units
+      for (int gq = 0; gq < 4; ++gq) {
         float a4[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float gv = acc[mb][0][4 * gq + j], uv = acc[mb][1][4 * gq + j];
           a4[j] = gv * sigmoidf_(gv) * uv;
         }
-        st_bf16x4(p.act + o, a4);
-      } else {
+        st_bf16x4(p.act + row + n0 + 32 * wn + 8 * gq + 4 * half, a4);  // intermediate units
+      }
+    } else {
+      // column of group gq of block nb; the epilogues that read memory issue
+      // all of the block row's loads before its first store (a store may
+      // alias a later load, so the compiler would otherwise wait for each
+      // load in turn)
+      auto col = [&](int gq, int nb) { return row + n0 + 64 * wn + 32 * nb + 8 * gq + 4 * half; };
+      if constexpr (kEpi == kEpiStoreBf16) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const size_t o = (size_t)m * p.ldc + n0 + 64 * wn + 32 * nb + c4;
-          float v4[4];
+        for (int gq = 0; gq < 4; ++gq)
 #pragma unroll
-          for (int j = 0; j < 4; ++j) v4[j] = acc[mb][nb][4 * gq + j];
-          if constexpr (kEpi == kEpiStoreBf16) {
-            st_bf16x4(static_cast<bf16*>(p.c) + o, v4);
-          } else if constexpr (kEpi == kEpiDGrad) {
-            float g4[4], u4[4];
-            ld_bf16x4(p.g + o, g4);
-            ld_bf16x4(p.u + o, u4);
+          for (int nb = 0; nb < 2; ++nb) {
+            const float v4[4] = {acc[mb][nb][4 * gq], acc[mb][nb][4 * gq + 1], acc[mb][nb][4 * gq + 2],
+                                 acc[mb][nb][4 * gq + 3]};
+            st_bf16x4(static_cast<bf16*>(p.c) + col(gq, nb), v4);
+          }
+      } else if constexpr (kEpi == kEpiDGrad) {
+        float g4[4][2][4], u4[4][2][4];
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            ld_bf16x4(p.g + col(gq, nb), g4[gq][nb]);
+            ld_bf16x4(p.u + col(gq, nb), u4[gq][nb]);
+          }
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              g4[j] *= v4[j];  // dG = dA * U * silu'(G)
-              u4[j] *= v4[j];  // dU = dA * silu(G)
+              const float v = acc[mb][nb][4 * gq + j];
+              g4[gq][nb][j] *= v;  // dG = dA * U * silu'(G)
+              u4[gq][nb][j] *= v;  // dU = dA * silu(G)
             }
-            st_bf16x4(p.g + o, g4);
-            st_bf16x4(p.u + o, u4);
-          } else {  // kEpiAccF32
-            float4* c = reinterpret_cast<float4*>(static_cast<float*>(p.c) + o);
-            float4 r = make_float4(v4[0], v4[1], v4[2], v4[3]);
-            if (p.accumulate) {
-              const float4 old = *c;
-              r = make_float4(old.x + r.x, old.y + r.y, old.z + r.z, old.w + r.w);
-            }
-            *c = r;
+            st_bf16x4(p.g + col(gq, nb), g4[gq][nb]);
+            st_bf16x4(p.u + col(gq, nb), u4[gq][nb]);
           }
+      } else {  // kEpiAccF32
+        float* c = static_cast<float*>(p.c);
+        float4 old[4][2];
+        if (p.accumulate) {
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) old[gq][nb] = *reinterpret_cast<const float4*>(c + col(gq, nb));
         }
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            float4 r = make_float4(acc[mb][nb][4 * gq], acc[mb][nb][4 * gq + 1], acc[mb][nb][4 * gq + 2],
+                                   acc[mb][nb][4 * gq + 3]);
+            if (p.accumulate) {
+              const float4 o = old[gq][nb];
+              r = make_float4(o.x + r.x, o.y + r.y, o.z + r.z, o.w + r.w);
+            }
+            *reinterpret_cast<float4*>(c + col(gq, nb)) = r;
+          }
       }
     }
   }
