@@ -278,14 +278,16 @@ int ulysses_ring_attn_fwd_step(const void* q, const void* k, const void* v, void
 
 /*
  * Bytes of workspace the ring backward needs: two floats per (rank, batch
- * row, head, token) (-D = -rowsum(dO * O) and lse in log2 units). Returns 0
- * for invalid arguments.
+ * row, head, token) (-D = -rowsum(dO * O) and lse in log2 units), then 2304
+ * bytes of tile-queue counters for the steps' persistent kernels (as in
+ * ulysses_attn_bwd_workspace_bytes). Returns 0 for invalid arguments.
  */
 size_t ulysses_ring_attn_bwd_workspace_bytes(int sp, int B, int Ns, int H, int d, int dtype);
 
 /*
  * Before the backward steps: -D = -rowsum(dO * O) and lse * log2(e) of every
- * query row into the workspace, from the forward's final o and lse.
+ * query row into the workspace, from the forward's final o and lse; also
+ * clears the workspace's queue counters.
  *   o, dout [sp][B][Ns][H][d] bf16; lse [sp][B][H][Ns] float.
  * Errors: as ulysses_ring_attn_fwd_step, plus ULY_EWORKSPACE.
  */
@@ -299,7 +301,10 @@ int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, const float* 
  * dS = P * (dP - D):
  *   dQ_r += scale dS K_j,  dK_j += scale dS^T Q_r,  dV_j += P^T dO_r.
  *   q, k, v, dout        [sp][B][Ns][H][d] bf16; lse the forward's final one
- *   workspace            as filled by ulysses_ring_attn_bwd_prepare
+ *   workspace            as filled by ulysses_ring_attn_bwd_prepare; the
+ *                        step's kernels claim tiles from its queue counters
+ *                        and leave them cleared for the next step, so steps
+ *                        on one workspace must not overlap
  *   dq_acc, dk_acc,      [sp][B][Ns][H][d] float running sums, indexed by the
  *   dv_acc               chunk they belong to (set at step 0, added to later)
  *   dq, dk, dv           [sp][B][Ns][H][d] bf16: a query chunk's dq is written
@@ -309,7 +314,7 @@ int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, const float* 
  * Errors: as ulysses_ring_attn_bwd_prepare.
  */
 int ulysses_ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* dout,
-                               const float* lse, const void* workspace, size_t workspace_bytes,
+                               const float* lse, void* workspace, size_t workspace_bytes,
                                float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
                                int step, int sp, int B, int Ns, int H, int d, int causal, int dtype,
                                void* stream);

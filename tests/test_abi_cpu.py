@@ -195,7 +195,7 @@ def test_ring_argument_errors():
     assert call(d=96) == EUNSUP
 
     need = lib.ulysses_ring_attn_bwd_workspace_bytes(4, 1, 8, 2, 64, 1)
-    assert need == 2 * 4 * 1 * 2 * 8 * 4
+    assert need == 2 * 4 * 1 * 2 * 8 * 4 + 2304  # two floats per row (256-byte aligned), then the queue counters
     assert lib.ulysses_ring_attn_bwd_workspace_bytes(4, 1, 8, 2, 64, 0) == 0
     prep = lib.ulysses_ring_attn_bwd_prepare
     assert prep(FAKE, FAKE, FAKE, FAKE, need - 1, 4, 1, 8, 2, 64, 1, None) == EWS

@@ -809,6 +809,7 @@ inline size_t sched_offset(size_t rows) { return (2 * rows * sizeof(float) + 255
 int* sched_counters(float* ws, size_t rows) {
   return reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + sched_offset(rows));
 }
+size_t bwd_workspace_bytes(size_t rows) { return sched_offset(rows) + kSchedBytes; }
 
 // The tile decode forms nslots * ndoc * max(units, kUnitGroup) in int, for
 // the dQ kernel's 256-query tiles and the dK/dV kernel's 128-key tiles.
@@ -913,7 +914,7 @@ int launch_attn_bwd_prepare_bf16(const void* o, const void* dout, const float* l
 }
 
 int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                         const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
+                         float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
                          void* dv, const AttnGeom& g, int sp, int B, int step, void* stream) {
   BwdArgs a;
   a.q = static_cast<const bf16*>(q);
@@ -941,7 +942,7 @@ int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void
   a.step = step;
   a.sp = sp;
   a.B = B;
-  a.sched = nullptr;  // one tile per workgroup (the ring's workspace has no queue counters)
+  a.sched = nullptr;
   BwdArgs aq = a;
   aq.nslots = (g.N + kDqBQ - 1) / kDqBQ;
   BwdArgs akv = a;
@@ -950,13 +951,26 @@ int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void
   const long long kvblocks = (long long)akv.nslots * a.units;
   const long long ug = a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup;
   if ((long long)aq.nslots * ug > 0x7fffffffLL || (long long)akv.nslots * ug > 0x7fffffffLL) return ULY_ESHAPE;
+  // Persistent launches, as in the Ulysses backward: the queue counters sit in
+  // the workspace's tail (the prepare call cleared them, each kernel leaves
+  // them cleared for the next step); tiles of rows whose chunk this step does
+  // not reach are claimed and passed over.
+  const int ncu = device_cu_count();
+  long long kvgrid = kvblocks, qgrid = qblocks;
+  if (ncu > 0) {
+    int* sched = sched_counters(delta, (size_t)g.G * g.Hl * g.N);
+    akv.sched = sched;
+    aq.sched = sched + kSchedDq;
+    kvgrid = kvblocks < ncu ? kvblocks : ncu;
+    qgrid = qblocks < ncu ? qblocks : ncu;
+  }
   hipStream_t st = (hipStream_t)stream;
   if (g.d == 64) {
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, true>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<64, true>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<64, true>), dim3((unsigned)kvgrid), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<64, true>), dim3((unsigned)qgrid), dim3(kDqThreads), 0, st, aq);
   } else {
-    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, true>), dim3((unsigned)kvblocks), dim3(kKvThreads), 0, st, akv);
-    hipLaunchKernelGGL((attn_dq_bf16_kernel<128, true>), dim3((unsigned)qblocks), dim3(kDqThreads), 0, st, aq);
+    hipLaunchKernelGGL((attn_dkdv_bf16_kernel<128, true>), dim3((unsigned)kvgrid), dim3(kKvThreads), 0, st, akv);
+    hipLaunchKernelGGL((attn_dq_bf16_kernel<128, true>), dim3((unsigned)qgrid), dim3(kDqThreads), 0, st, aq);
   }
   return launch_status();
 }
@@ -968,7 +982,7 @@ extern "C" size_t ulysses_attn_bwd_workspace_bytes(int sp, int B, int N, int Hl,
   if (!uly_host::dtype_ok(dtype) || !uly_host::head_dim_ok(d)) return 0;
   // -D = -rowsum(dO * O) and lse in log2 units: two floats per (rank, batch row, head, token),
   // then the tile-queue counters of the dK/dV and dQ kernels.
-  return uly_host::sched_offset((size_t)sp * B * Hl * N) + uly_host::kSchedBytes;
+  return uly_host::bwd_workspace_bytes((size_t)sp * B * Hl * N);
 }
 
 extern "C" int ulysses_attn_bwd(const void* q, const void* k, const void* v, const void* o,

@@ -46,8 +46,13 @@ int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const
 // Ring attention steps (bf16): rows g = chunk * B + b of Ns tokens, H heads.
 int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* o_acc, float* lse,
                          const AttnGeom& a, int sp, int B, int step, void* stream);
+// delta: the workspace the ring prepare call filled (ring_bwd_workspace_bytes
+// of it), whose queue counters the step's persistent kernels claim from.
 int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,
-                         const float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
+                         float* delta, float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk,
                          void* dv, const AttnGeom& a, int sp, int B, int step, void* stream);
+// Bytes of a backward workspace over `rows` (rank, batch row, head, token)
+// rows: -D and lse in log2 units, then the two kernels' queue counters.
+size_t bwd_workspace_bytes(size_t rows);
 
 }  // namespace uly_host

@@ -57,8 +57,9 @@ extern "C" int ulysses_ring_attn_fwd_step(const void* q, const void* k, const vo
 
 extern "C" size_t ulysses_ring_attn_bwd_workspace_bytes(int sp, int B, int Ns, int H, int d, int dtype) {
   if (check_ring(0, sp, B, Ns, H, d, dtype) != ULY_OK) return 0;
-  // D and lse in log2 units: two floats per (rank, batch row, head, token)
-  return 2 * (size_t)sp * B * H * Ns * sizeof(float);
+  // -D and lse in log2 units: two floats per (rank, batch row, head, token),
+  // then the queue counters of the steps' persistent kernels
+  return uly_host::bwd_workspace_bytes((size_t)sp * B * H * Ns);
 }
 
 extern "C" int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, const float* lse, void* workspace,
@@ -70,11 +71,11 @@ extern "C" int ulysses_ring_attn_bwd_prepare(const void* o, const void* dout, co
   if (!workspace || workspace_bytes < ulysses_ring_attn_bwd_workspace_bytes(sp, B, Ns, H, d, dtype))
     return ULY_EWORKSPACE;
   return uly_host::launch_attn_bwd_prepare_bf16(o, dout, lse, static_cast<float*>(workspace),
-                                                ring_geom(sp, B, Ns, H, d, 1), stream, false);
+                                                ring_geom(sp, B, Ns, H, d, 1), stream, true);
 }
 
 extern "C" int ulysses_ring_attn_bwd_step(const void* q, const void* k, const void* v, const void* dout,
-                                          const float* lse, const void* workspace, size_t workspace_bytes,
+                                          const float* lse, void* workspace, size_t workspace_bytes,
                                           float* dq_acc, float* dk_acc, float* dv_acc, void* dq, void* dk, void* dv,
                                           int step, int sp, int B, int Ns, int H, int d, int causal, int dtype,
                                           void* stream) {
@@ -83,7 +84,7 @@ extern "C" int ulysses_ring_attn_bwd_step(const void* q, const void* k, const vo
   if (rc != ULY_OK) return rc;
   if (!workspace || workspace_bytes < ulysses_ring_attn_bwd_workspace_bytes(sp, B, Ns, H, d, dtype))
     return ULY_EWORKSPACE;
-  return uly_host::launch_ring_bwd_bf16(q, k, v, dout, lse, static_cast<const float*>(workspace), dq_acc, dk_acc,
+  return uly_host::launch_ring_bwd_bf16(q, k, v, dout, lse, static_cast<float*>(workspace), dq_acc, dk_acc,
                                         dv_acc, dq, dk, dv, ring_geom(sp, B, Ns, H, d, causal), sp, B, step,
                                         stream);
 }
