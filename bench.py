@@ -192,6 +192,7 @@ def make_ring_buffers(w: workloads.Workload, dev):
         "accs": [f32() for _ in range(3)],
         "ws": torch.empty(uly.ulysses_ring_attn_bwd_workspace_bytes(w.sp, w.B, w.Ns, w.H, w.d),
                           dtype=torch.uint8, device=dev),
+        "fws": torch.empty(uly.ulysses_attn_fwd_workspace_bytes(), dtype=torch.uint8, device=dev),
     }
 
 
@@ -202,7 +203,8 @@ def ring_step(w, bufs, timer=None):
     dq, dk, dv = bufs["grads"]
     dqa, dka, dva = bufs["accs"]
     for i in range(w.sp):
-        run("ring_fwd_step", lambda: uly.ulysses_ring_attn_fwd_step(q, k, v, i, w.causal, o, o_acc, lse))
+        run("ring_fwd_step", lambda: uly.ulysses_ring_attn_fwd_step(q, k, v, i, w.causal, o, o_acc, lse,
+                                                                     bufs["fws"]))
     run("ring_bwd_prepare", lambda: uly.ulysses_ring_attn_bwd_prepare(o, do, lse, ws))
     for i in range(w.sp):
         run("ring_bwd_step", lambda: uly.ulysses_ring_attn_bwd_step(q, k, v, do, lse, ws, i, w.causal,

@@ -277,6 +277,19 @@ int ulysses_ring_attn_fwd_step(const void* q, const void* k, const void* v, void
                                int dtype, void* stream);
 
 /*
+ * ulysses_ring_attn_fwd_step as a persistent launch, like ulysses_attn_fwd_ws:
+ * the caller lends ulysses_attn_fwd_workspace_bytes() (1152) bytes of device
+ * memory for the step's tile-queue counters (cleared on the stream before the
+ * kernel; contents on entry ignored; steps that share one workspace must not
+ * overlap). Same results, bit for bit.
+ * Errors: as ulysses_ring_attn_fwd_step; ULY_EWORKSPACE (workspace NULL or
+ * too small).
+ */
+int ulysses_ring_attn_fwd_step_ws(const void* q, const void* k, const void* v, void* o, float* o_acc,
+                                  float* lse, void* workspace, size_t workspace_bytes, int step, int sp,
+                                  int B, int Ns, int H, int d, int causal, int dtype, void* stream);
+
+/*
  * Bytes of workspace the ring backward needs: two floats per (rank, batch
  * row, head, token) (-D = -rowsum(dO * O) and lse in log2 units), then 2304
  * bytes of tile-queue counters for the steps' persistent kernels (as in

@@ -33,7 +33,8 @@ def test_library_exports_every_declared_function():
         "ulysses_attn_fwd_ws", "ulysses_attn_fwd_workspace_bytes",
         "ulysses_attn_bwd_workspace_bytes", "ulysses_status_string", "ulysses_attn_bwd_noalloc",
         "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
-        "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
+        "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_fwd_step_ws",
+        "ulysses_ring_attn_bwd_workspace_bytes", "ulysses_ring_attn_bwd_prepare",
         "ulysses_ring_attn_bwd_step", "ulysses_sp_loss_workspace_bytes", "ulysses_sp_loss",
         "ulysses_tiled_mlp_workspace_bytes", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd",
     }
@@ -188,6 +189,12 @@ def test_ring_argument_errors():
                  a["causal"], a["dtype"], None)
 
     assert f(FAKE, FAKE, FAKE, FAKE, None, FAKE, 0, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL  # o_acc
+    fws = lib.ulysses_ring_attn_fwd_step_ws
+    fneed = lib.ulysses_attn_fwd_workspace_bytes()
+    assert fws(*([FAKE] * 6), None, fneed, 0, 4, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert fws(*([FAKE] * 6), FAKE, fneed - 1, 0, 4, 1, 8, 2, 64, 1, 1, None) == EWS
+    assert fws(*([FAKE] * 6), FAKE, fneed, 4, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL  # step
+    assert fws(*([FAKE] * 5), None, FAKE, fneed, 0, 4, 1, 8, 2, 64, 1, 1, None) == EINVAL  # lse
     assert call(step=-1) == EINVAL
     assert call(step=4) == EINVAL  # steps are 0 .. sp-1
     assert call(Ns=0) == EINVAL

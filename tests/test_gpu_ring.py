@@ -65,6 +65,25 @@ def test_ring_steps_against_oracle(sp, B, Ns, H, d, causal):
     assert_rel(ring.stitch(f64(o.cpu())), O_full, TOL_BF16_O, "o vs whole-sequence attention")
 
 
+@pytest.mark.parametrize("sp,B,Ns,H,d,causal", [
+    (2, 1, 300, 2, 128, True),
+    (4, 2, 130, 2, 64, True),
+    (3, 1, 257, 1, 128, False),
+])
+def test_ring_fwd_persistent_equals_one_tile_per_workgroup(sp, B, Ns, H, d, causal):
+    """The forward steps' persistent launch (ulysses_ring_attn_fwd_step_ws) computes
+    every tile whole in one workgroup: the same bits as one workgroup per tile,
+    whatever the workspace held on entry, with one workspace serving every step."""
+    say("ring fwd persistent", sp, B, Ns, H, d, causal)
+    dev = device()
+    q, k, v, _ = (t.to(dev) for t in workloads.qkv_do((sp, B, Ns, H, d), 50 + sp, "bf16"))
+    o1, l1 = uly.ring_attn_fwd(q, k, v, causal)
+    fws = torch.full((uly.ulysses_attn_fwd_workspace_bytes(),), 0xFF, dtype=torch.uint8, device=dev)
+    o2, l2 = uly.ring_attn_fwd(q, k, v, causal, workspace=fws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_ring_long_workload_sampled():
     """The long workload's sequence (131072 tokens, 32 heads, d = 128, inputs
     scaled by 0.5) as a ring of 8 chunks, all steps: sampled query rows and

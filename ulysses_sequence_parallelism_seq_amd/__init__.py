@@ -81,6 +81,7 @@ def library() -> ctypes.CDLL:
         lib.ulysses_attn_bwd_prepare.argtypes = [vp] * 4 + [sz] + [i] * 6 + [vp]
         lib.ulysses_attn_bwd_prepared.argtypes = [vp] * 9 + [sz, vp] + [i] * 9 + [vp]
         lib.ulysses_ring_attn_fwd_step.argtypes = [vp] * 6 + [i] * 8 + [vp]
+        lib.ulysses_ring_attn_fwd_step_ws.argtypes = [vp] * 7 + [sz] + [i] * 8 + [vp]
         lib.ulysses_ring_attn_bwd_workspace_bytes.argtypes = [i] * 6
         lib.ulysses_ring_attn_bwd_workspace_bytes.restype = sz
         lib.ulysses_ring_attn_bwd_prepare.argtypes = [vp] * 4 + [sz] + [i] * 6 + [vp]
@@ -98,7 +99,8 @@ def library() -> ctypes.CDLL:
                      "ulysses_head_to_seq_n", "ulysses_attn_fwd", "ulysses_attn_fwd_ws",
                      "ulysses_attn_bwd",
                      "ulysses_attn_bwd_noalloc", "ulysses_attn_bwd_prepare", "ulysses_attn_bwd_prepared",
-                     "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
+                     "ulysses_ring_attn_fwd_step", "ulysses_ring_attn_fwd_step_ws",
+                     "ulysses_ring_attn_bwd_prepare", "ulysses_ring_attn_bwd_step",
                      "ulysses_sp_loss", "ulysses_tiled_mlp_fwd", "ulysses_tiled_mlp_bwd"):
             getattr(lib, name).restype = i
         _lib = lib
@@ -407,8 +409,11 @@ def _ring_shape(q):
     return tuple(q.shape)
 
 
-def ulysses_ring_attn_fwd_step(q, k, v, step: int, causal: bool = True, o=None, o_acc=None, lse=None):
-    """One forward ring step; returns (o, o_acc, lse). Pass the previous step's o_acc and lse back in."""
+def ulysses_ring_attn_fwd_step(q, k, v, step: int, causal: bool = True, o=None, o_acc=None, lse=None,
+                               workspace=None):
+    """One forward ring step; returns (o, o_acc, lse). Pass the previous step's o_acc and lse back in.
+    With a workspace (ulysses_attn_fwd_workspace_bytes() bytes) the step runs as the
+    persistent launch of ulysses_ring_attn_fwd_step_ws (same bits)."""
     sp, B, Ns, H, d = _ring_shape(q)
     for t in (k, v):
         if t.shape != q.shape or t.dtype != q.dtype:
@@ -422,16 +427,23 @@ def ulysses_ring_attn_fwd_step(q, k, v, step: int, causal: bool = True, o=None, 
     _expect(o_acc, q.shape, torch.float32, "o_acc")
     _expect(lse, (sp, B, H, Ns), torch.float32, "lse")
     _require_device(q, k, v, o, o_acc, lse)
-    _check("ulysses_ring_attn_fwd_step", library().ulysses_ring_attn_fwd_step(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_acc), _ptr(lse), int(step), sp, B, Ns, H, d,
-        int(bool(causal)), ULY_BF16, _stream(q)))
+    if workspace is None:
+        _check("ulysses_ring_attn_fwd_step", library().ulysses_ring_attn_fwd_step(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_acc), _ptr(lse), int(step), sp, B, Ns, H, d,
+            int(bool(causal)), ULY_BF16, _stream(q)))
+    else:
+        _require_device(q, workspace)
+        _check("ulysses_ring_attn_fwd_step_ws", library().ulysses_ring_attn_fwd_step_ws(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(o_acc), _ptr(lse), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), int(step), sp, B, Ns, H, d,
+            int(bool(causal)), ULY_BF16, _stream(q)))
     return o, o_acc, lse
 
 
-def ring_attn_fwd(q, k, v, causal: bool = True, o=None, o_acc=None, lse=None):
+def ring_attn_fwd(q, k, v, causal: bool = True, o=None, o_acc=None, lse=None, workspace=None):
     """All sp forward ring steps in order; returns (o, lse)."""
     for step in range(q.shape[0]):
-        o, o_acc, lse = ulysses_ring_attn_fwd_step(q, k, v, step, causal, o, o_acc, lse)
+        o, o_acc, lse = ulysses_ring_attn_fwd_step(q, k, v, step, causal, o, o_acc, lse, workspace)
     return o, lse
 
 

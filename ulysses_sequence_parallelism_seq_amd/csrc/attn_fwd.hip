@@ -414,7 +414,7 @@ int launch_attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, f
 }
 
 int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* o_acc, float* lse,
-                         const AttnGeom& g, int sp, int B, int step, void* stream) {
+                         const AttnGeom& g, int sp, int B, int step, void* stream, int* sched) {
   FwdArgs a;
   a.q = static_cast<const bf16*>(q);
   a.k = static_cast<const bf16*>(k);
@@ -433,15 +433,24 @@ int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, f
   a.step = step;
   a.sp = sp;
   a.B = B;
-  a.sched = nullptr;  // one tile per workgroup
+  a.sched = nullptr;
   const long long blocks = (long long)a.nq_slots * a.units;
   const long long span = (long long)a.nq_slots * (a.units > uly::kUnitGroup ? a.units : uly::kUnitGroup);
   if (span > 0x7fffffffLL) return ULY_ESHAPE;
   hipStream_t st = (hipStream_t)stream;
+  long long grid = blocks;
+  // persistent when the caller lends the counters (tiles of ranks this step
+  // does not reach are claimed and passed over), else one tile per workgroup
+  const int ncu = sched ? device_cu_count() : 0;
+  if (ncu > 0) {
+    hipLaunchKernelGGL(sched_clear_kernel, dim3(1), dim3(64), 0, st, sched);
+    a.sched = sched;
+    grid = blocks < ncu ? blocks : ncu;
+  }
   if (g.d == 64)
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
   else
-    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), dim3((unsigned)blocks), dim3(kThreads), 0, st, a);
+    hipLaunchKernelGGL((attn_fwd_bf16_kernel<128, true>), dim3((unsigned)grid), dim3(kThreads), 0, st, a);
   return launch_status();
 }
 

@@ -44,8 +44,10 @@ int launch_attn_bwd_main_bf16(const void* q, const void* k, const void* v, const
                               const AttnGeom& a, void* stream);
 
 // Ring attention steps (bf16): rows g = chunk * B + b of Ns tokens, H heads.
+// sched: the forward's queue counters (ulysses_attn_fwd_workspace_bytes) for
+// a persistent launch, or nullptr for one workgroup per tile.
 int launch_ring_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* o_acc, float* lse,
-                         const AttnGeom& a, int sp, int B, int step, void* stream);
+                         const AttnGeom& a, int sp, int B, int step, void* stream, int* sched);
 // delta: the workspace the ring prepare call filled (ring_bwd_workspace_bytes
 // of it), whose queue counters the step's persistent kernels claim from.
 int launch_ring_bwd_bf16(const void* q, const void* k, const void* v, const void* dout, const float* lse,

@@ -52,7 +52,18 @@ extern "C" int ulysses_ring_attn_fwd_step(const void* q, const void* k, const vo
   const int rc = check_ring(step, sp, B, Ns, H, d, dtype);
   if (rc != ULY_OK) return rc;
   return uly_host::launch_ring_fwd_bf16(q, k, v, o, o_acc, lse, ring_geom(sp, B, Ns, H, d, causal), sp, B, step,
-                                        stream);
+                                        stream, nullptr);
+}
+
+extern "C" int ulysses_ring_attn_fwd_step_ws(const void* q, const void* k, const void* v, void* o, float* o_acc,
+                                             float* lse, void* workspace, size_t workspace_bytes, int step, int sp,
+                                             int B, int Ns, int H, int d, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !o_acc || !lse) return ULY_EINVAL;
+  const int rc = check_ring(step, sp, B, Ns, H, d, dtype);
+  if (rc != ULY_OK) return rc;
+  if (!workspace || workspace_bytes < ulysses_attn_fwd_workspace_bytes()) return ULY_EWORKSPACE;
+  return uly_host::launch_ring_fwd_bf16(q, k, v, o, o_acc, lse, ring_geom(sp, B, Ns, H, d, causal), sp, B, step,
+                                        stream, static_cast<int*>(workspace));
 }
 
 extern "C" size_t ulysses_ring_attn_bwd_workspace_bytes(int sp, int B, int Ns, int H, int d, int dtype) {
