@@ -69,7 +69,7 @@ extern "C" {
  * 16-byte aligned.
  * Errors: ULY_EINVAL (null, size <= 0, overlap, misaligned); ULY_ESHAPE when
  * N % sp != 0, H % sp != 0, sp > 65535, sp * B >= 2^32, or one shard's
- * output counts 2^32 - 1024 or more 16-byte chunks: (N/sp) * (H/sp) * d *
+ * output counts 2^32 - 512 or more 16-byte chunks: (N/sp) * (H/sp) * d *
  * esize / 16 here, N * (H/sp) * d * esize / 16 for ulysses_head_to_seq
  * (esize = 4 for ULY_F32, 2 for ULY_BF16); ULY_EUNSUPPORTED (dtype, d);
  * ULY_EHIP.
